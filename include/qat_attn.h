@@ -1,0 +1,155 @@
+/*
+ * qat_attn.h -- C ABI of the MI355X (gfx950) quantization-aware attention
+ * library libqat_attn.so.
+ *
+ * What it computes.  Fake-quant ("QAT") attention as in the FastVideo
+ * attn_qat_train.py source page (functions _attn_fwd_inner, _attn_fwd,
+ * _attn_bwd_preprocess, _attn_bwd_dkdv_cross, _attn_bwd_dq_cross and the
+ * autograd wrapper _attention): the forward fake-quantizes the probability
+ * tile P to fp8 (one absmax scale per query row and per group of
+ * QAT_ATTN_P_GROUP key columns), keeps the quantized output O, a
+ * high-precision straight-through copy O_hp and the log-sum-exp; the
+ * backward rematerialises S and P from the log-sum-exp (the idea raised in
+ * the "support for pytorch autograd" discussion) and returns straight-through
+ * gradients dQ, dK, dV through every quantizer.
+ *
+ *   S    = sm_scale * Q^ K^T          (causal: keys j > query i masked)
+ *   lse  = log sum_j exp(S)            (natural log, fp32)
+ *   P    = exp(S - lse);  P^ = FQ(P)   per row, per QAT_ATTN_P_GROUP columns
+ *   O_hp = P V^,   O = P^ V^
+ *   Delta = rowsum(dO o O_hp), dS = P o (dO V^T - Delta)
+ *   dV = P^T dO,  dQ = sm_scale dS K^,  dK = sm_scale dS^T Q^
+ *
+ * FQ(x) over a group: a = max|x|, s = fp32(a/FMAX), r = fp32(FMAX/a),
+ * code = fp8 round-to-nearest-even, saturating (x*r), x^ = fp32(code*s);
+ * an all-zero group gives zeros.  FMAX = 448 (e4m3fn) or 57344 (e5m2).
+ *
+ * Conventions shared by every entry point.
+ *  - All tensor pointers are DEVICE pointers on the current HIP device,
+ *    contiguous, layout [B, H, N, D] (row-major; D fastest), 16-byte aligned.
+ *  - Storage dtype of q, k, v, dout, o, o_hp, dq, dk, dv is dims->dtype
+ *    (bf16 or fp16); lse and v_scale are fp32.
+ *  - `stream` is a hipStream_t (NULL: the default stream).  Every call only
+ *    enqueues work on that stream; none synchronises, none allocates.
+ *  - The caller owns every buffer, including the workspace.  Outputs are
+ *    overwritten, never accumulated into.
+ *  - Errors: validation happens before any launch and returns a nonzero
+ *    status with nothing enqueued.  QAT_EHIP reports a failed launch.
+ *  - Results are deterministic: no atomics, fixed reduction orders.
+ */
+#ifndef QAT_ATTN_H
+#define QAT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define QAT_OK 0
+#define QAT_EINVAL 1        /* null pointer, bad size, unknown flag bit      */
+#define QAT_EUNSUPPORTED 2  /* valid request this build does not implement    */
+#define QAT_EWORKSPACE 3    /* workspace pointer null or smaller than needed  */
+#define QAT_EHIP 4          /* a kernel launch failed                         */
+
+/* storage dtypes */
+#define QAT_DTYPE_BF16 0
+#define QAT_DTYPE_FP16 1
+
+/* quant_flags bits */
+#define QAT_P_QUANT     (1u << 0) /* fake-quant P (else O == O_hp)                      */
+#define QAT_P_E5M2      (1u << 1) /* P grid e5m2 (else e4m3fn)                          */
+#define QAT_QKV_QUANT   (1u << 2) /* per-token e4m3fn fake quant of Q, K, V over D      */
+#define QAT_V_FP8_E5M2  (1u << 3) /* v holds e5m2 codes (uint8) + v_scale[B,H,D] fp32  */
+
+#define QAT_ATTN_P_GROUP 64       /* key columns per P-quant scale (absolute columns)   */
+
+typedef struct qat_attn_dims {
+    int32_t B, H;      /* batch, heads                                           */
+    int32_t Nq, Nkv;   /* query and key/value sequence lengths (Nkv may != Nq)   */
+    int32_t D;         /* head dim: 64 or 128                                    */
+    int32_t dtype;     /* QAT_DTYPE_BF16 or QAT_DTYPE_FP16                        */
+} qat_attn_dims;
+
+/*
+ * Forward (FastVideo attn_qat_train.py: _attention.forward driving the
+ * fake_quantize_q / fake_quantize_kv pre-pass and _attn_fwd / _attn_fwd_inner).
+ *
+ *  q [B,H,Nq,D], k [B,H,Nkv,D]: dtype.
+ *  v [B,H,Nkv,D]: dtype, or uint8 e5m2 codes with QAT_V_FP8_E5M2, in which
+ *     case v_scale [B,H,D] (fp32) gives V^ = code * v_scale[b,h,d]; v_scale
+ *     must be NULL otherwise.
+ *  sm_scale: softmax scale (> 0, finite).  causal: nonzero for the causal
+ *     mask (requires Nq == Nkv, top-left aligned, diagonal kept).
+ *  o, o_hp [B,H,Nq,D] (dtype): quantized-P output and straight-through output.
+ *  lse [B,H,Nq] (fp32): natural-log log-sum-exp of each query row.
+ *  workspace: device scratch of at least qat_attn_workspace_bytes(dims,
+ *     flags, 0) bytes (may be NULL when that is 0).
+ *
+ * Returns QAT_EINVAL (null/size/flag errors, v_scale presence not matching
+ * the flag), QAT_EUNSUPPORTED (D not 64/128, causal with Nq != Nkv,
+ * QAT_V_FP8_E5M2 together with QAT_QKV_QUANT or with fp16), QAT_EWORKSPACE,
+ * QAT_EHIP, else QAT_OK.
+ */
+int qat_attn_fwd(const qat_attn_dims* dims, const void* q, const void* k, const void* v,
+                 const float* v_scale, float sm_scale, int causal, uint32_t quant_flags,
+                 void* o, void* o_hp, float* lse, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/*
+ * Backward (FastVideo attn_qat_train.py: _attention.backward with
+ * _attn_bwd_preprocess, _attn_bwd_dkdv_cross, _attn_bwd_dq_cross).
+ *
+ * Takes the same q, k, v, v_scale, sm_scale, causal and quant_flags as the
+ * forward, the forward's o_hp and lse, and dout = dL/dO [B,H,Nq,D] (dtype).
+ * With QAT_QKV_QUANT the inputs are fake-quantized again exactly as in the
+ * forward (bit-identical), and the gradients are evaluated there.
+ * Writes dq [B,H,Nq,D], dk, dv [B,H,Nkv,D] (dtype; dv is the gradient with
+ * respect to the dequantized V^ when V is fp8) as straight-through gradients
+ * of the un-quantized inputs.  Delta = rowsum(dout o o_hp) is kept in the
+ * workspace (>= qat_attn_workspace_bytes(dims, flags, 1) bytes).
+ * Errors as for qat_attn_fwd.
+ */
+int qat_attn_bwd(const qat_attn_dims* dims, const void* q, const void* k, const void* v,
+                 const float* v_scale, const void* o_hp, const float* lse, const void* dout,
+                 float sm_scale, int causal, uint32_t quant_flags,
+                 void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/* Workspace bytes needed by the forward (pass 0) or the backward (pass 1);
+ * 0 for invalid dims. */
+size_t qat_attn_workspace_bytes(const qat_attn_dims* dims, uint32_t quant_flags, int pass);
+
+/*
+ * Per-channel e5m2 quantization of V for the fp8-V path (the e5m2 value path
+ * of _attn_fwd in the FastVideo source, with one absmax scale per
+ * (b, h, d) over the Nkv tokens).  v [B,H,Nkv,D] dtype -> codes [B,H,Nkv,D]
+ * uint8 and v_scale [B,H,D] fp32, by FQ with FMAX = 57344.
+ * Errors: QAT_EINVAL, QAT_EUNSUPPORTED (D), QAT_EHIP.
+ */
+int qat_quant_v_fp8(const qat_attn_dims* dims, const void* v, uint8_t* codes, float* v_scale,
+                    void* stream);
+
+/*
+ * FQ of a row-major fp32 matrix x [rows, cols] with one scale per row and
+ * per `group` absolute columns, through the same device code the attention
+ * kernels use (the fake_quantize call of _attn_fwd_inner).  fmt: 0 = e4m3fn,
+ * 1 = e5m2.  Writes codes [rows, cols] uint8, scales [rows, ceil(cols/group)]
+ * fp32 and xhat [rows, cols] fp32 (any of the three may be NULL).
+ * Errors: QAT_EINVAL (x null, rows/cols/group <= 0, fmt not 0/1), QAT_EHIP.
+ */
+int qat_fake_quant_rows(const float* x, int32_t rows, int32_t cols, int32_t group, int32_t fmt,
+                        uint8_t* codes, float* scales, float* xhat, void* stream);
+
+/* QAT_ATTN_P_GROUP as compiled into the kernels. */
+int qat_attn_p_group(void);
+
+/* Static description of a status code. */
+const char* qat_attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QAT_ATTN_H */

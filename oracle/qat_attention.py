@@ -207,8 +207,10 @@ def backward_head(qh, kh, vh, do, sm_scale, causal=False, p_quant=True, p_fmt="e
 
     ``do`` is dO [Nq, D].  Returns ``(dQ[q_rows], dK[k_rows], dV[k_rows])``
     (all rows when None).  The sums over query rows that make dK and dV are
-    split into row blocks only to bound memory; within a block every step is
-    the plain definition.
+    split into row blocks only to bound memory, and only the columns of P
+    that the requested keys need are formed (with their whole P-quant group,
+    since a group's scale depends on all of its columns); within a block
+    every step is the plain definition.
     """
     Nq, D = qh.shape
     Nkv = kh.shape[0]
@@ -220,20 +222,26 @@ def backward_head(qh, kh, vh, do, sm_scale, causal=False, p_quant=True, p_fmt="e
     dQ = np.zeros((Nq, D))
     need_dq = np.zeros(Nq, dtype=bool)
     need_dq[q_rows] = True
+    groups = np.unique(k_rows // group)
     for b0 in range(0, Nq, row_block):
         r = np.arange(b0, min(Nq, b0 + row_block))
         S = _scores(qh, kh, sm_scale, causal, r)
         P, _ = _softmax_rows(S)
-        Ph = _p_hat(P, p_quant, p_fmt, group)
         O_hp = P @ vh
         Delta = np.sum(do[r] * O_hp, axis=1)                  # rowsum(dO o O_hp)
-        dP = do[r] @ vh.T
-        dS = P * (dP - Delta[:, None])
+        Ph = np.zeros_like(P)                                 # P^, needed groups only
+        for g in groups:
+            c = slice(g * group, min(Nkv, (g + 1) * group))
+            Ph[:, c] = _p_hat(P[:, c], p_quant, p_fmt, group)
+        dP = do[r] @ vh[k_rows].T                             # dP = dO V^T (needed keys)
+        dS = P[:, k_rows] * (dP - Delta[:, None])             # dS = P o (dP - Delta)
         dV += Ph[:, k_rows].T @ do[r]                         # dV = P^T dO
-        dK += float(sm_scale) * (dS[:, k_rows].T @ qh[r])     # dK = scale dS^T Q
+        dK += float(sm_scale) * (dS.T @ qh[r])                # dK = scale dS^T Q
         sel = need_dq[r]
         if sel.any():
-            dQ[r[sel]] = float(sm_scale) * (dS[sel] @ kh)     # dQ = scale dS K
+            dP_q = do[r[sel]] @ vh.T
+            dS_q = P[sel] * (dP_q - Delta[sel, None])
+            dQ[r[sel]] = float(sm_scale) * (dS_q @ kh)        # dQ = scale dS K
     return dQ[q_rows], dK, dV
 
 

@@ -3,17 +3,15 @@ straight-through backward).  Hand-written HIP kernels for gfx950 behind the C
 ABI declared in ``include/qat_attn.h``; this package holds the ctypes binding
 (``ops``) and the seeded synthetic workloads (``workloads``).
 
-The binding is imported lazily so that host-only code (workload generation)
+Submodules are imported lazily so that host-only code (workload generation)
 does not need the built library.
 """
-__all__ = ["ops", "workloads"]
+import importlib
+
+__all__ = ["ops", "workloads", "build"]
 
 
 def __getattr__(name):
-    if name == "ops":
-        from . import ops
-        return ops
-    if name == "workloads":
-        from . import workloads
-        return workloads
+    if name in __all__:
+        return importlib.import_module(f"{__name__}.{name}")
     raise AttributeError(name)

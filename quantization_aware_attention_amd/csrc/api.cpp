@@ -1,0 +1,211 @@
+// C ABI of libqat_attn.so (declared in include/qat_attn.h): argument
+// validation, workspace layout and kernel dispatch.  Every check runs before
+// the first launch, so an error return means nothing was enqueued.
+#include "../../include/qat_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "launch.hpp"
+
+namespace {
+
+constexpr uint32_t KNOWN_FLAGS = QAT_P_QUANT | QAT_P_E5M2 | QAT_QKV_QUANT | QAT_V_FP8_E5M2;
+constexpr size_t ALIGN = 256;
+
+inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Workspace layout (each piece 256-byte aligned, in this order):
+//   bwd: delta fp32 [B,H,Nq]; p_amax fp32 [B,H,ceil(Nkv/64),Nq] (P quant only)
+//   fwd and bwd: q^, k^, v^ (dtype) when Q/K/V quantization is on
+struct Layout {
+  size_t delta = 0, amax = 0, qh = 0, kh = 0, vh = 0, total = 0;
+};
+
+Layout layout(const qat_attn_dims& d, uint32_t flags, int pass) {
+  Layout L;
+  const size_t BH = (size_t)d.B * d.H;
+  size_t off = 0;
+  if (pass == 1) {
+    L.delta = off;
+    off += align_up(BH * d.Nq * sizeof(float));
+    if (flags & QAT_P_QUANT) {
+      L.amax = off;
+      const size_t ng = ((size_t)d.Nkv + QAT_ATTN_P_GROUP - 1) / QAT_ATTN_P_GROUP;
+      off += align_up(BH * ng * d.Nq * sizeof(float));
+    }
+  }
+  if (flags & QAT_QKV_QUANT) {
+    L.qh = off;
+    off += align_up(BH * d.Nq * d.D * 2);
+    L.kh = off;
+    off += align_up(BH * d.Nkv * d.D * 2);
+    L.vh = off;
+    off += align_up(BH * d.Nkv * d.D * 2);
+  }
+  L.total = off;
+  return L;
+}
+
+// Shared validation.  Returns QAT_OK and sets *empty when there is no work.
+int check_common(const qat_attn_dims* dims, float sm_scale, int causal, uint32_t flags,
+                 const float* v_scale, bool* empty) {
+  if (!dims) return QAT_EINVAL;
+  const qat_attn_dims& d = *dims;
+  if (d.B < 0 || d.H < 0 || d.Nq < 0 || d.Nkv < 0 || d.D <= 0) return QAT_EINVAL;
+  if (d.dtype != QAT_DTYPE_BF16 && d.dtype != QAT_DTYPE_FP16) return QAT_EINVAL;
+  if (flags & ~KNOWN_FLAGS) return QAT_EINVAL;
+  if ((flags & QAT_P_E5M2) && !(flags & QAT_P_QUANT)) return QAT_EINVAL;
+  if (!(std::isfinite(sm_scale) && sm_scale > 0.0f)) return QAT_EINVAL;
+  const bool vfp8 = (flags & QAT_V_FP8_E5M2) != 0;
+  if (vfp8 != (v_scale != nullptr)) return QAT_EINVAL;
+  if (d.D != 64 && d.D != 128) return QAT_EUNSUPPORTED;
+  if (causal && d.Nq != d.Nkv) return QAT_EUNSUPPORTED;
+  if (vfp8 && (d.dtype != QAT_DTYPE_BF16 || (flags & QAT_QKV_QUANT))) return QAT_EUNSUPPORTED;
+  if ((long long)d.B * d.H > 65535) return QAT_EUNSUPPORTED;
+  *empty = (d.B == 0 || d.H == 0 || d.Nq == 0);
+  if (!*empty && d.Nkv == 0) return QAT_EINVAL;   // softmax over no keys
+  return QAT_OK;
+}
+
+int check_ptr(const void* p) { return (p && aligned16(p)) ? QAT_OK : QAT_EINVAL; }
+
+qat::Shape shape_of(const qat_attn_dims& d) { return qat::Shape{d.B, d.H, d.Nq, d.Nkv, d.D, d.dtype}; }
+
+int pfmt_of(uint32_t flags) {
+  if (!(flags & QAT_P_QUANT)) return -1;
+  return (flags & QAT_P_E5M2) ? 1 : 0;
+}
+
+#define QAT_TRY(expr)                                  \
+  do {                                                 \
+    if ((expr) != hipSuccess) return QAT_EHIP;         \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t qat_attn_workspace_bytes(const qat_attn_dims* dims, uint32_t quant_flags, int pass) {
+  if (!dims || (pass != 0 && pass != 1)) return 0;
+  const qat_attn_dims& d = *dims;
+  if (d.B < 0 || d.H < 0 || d.Nq < 0 || d.Nkv < 0 || d.D <= 0) return 0;
+  return layout(d, quant_flags, pass).total;
+}
+
+int qat_attn_fwd(const qat_attn_dims* dims, const void* q, const void* k, const void* v,
+                 const float* v_scale, float sm_scale, int causal, uint32_t quant_flags,
+                 void* o, void* o_hp, float* lse, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  bool empty = false;
+  int rc = check_common(dims, sm_scale, causal, quant_flags, v_scale, &empty);
+  if (rc != QAT_OK) return rc;
+  if (empty) return QAT_OK;
+  const void* need[] = {q, k, v, o, o_hp, lse};
+  for (const void* p : need)
+    if ((rc = check_ptr(p)) != QAT_OK) return rc;
+  if (v_scale && !aligned16(v_scale)) return QAT_EINVAL;
+  const qat_attn_dims& d = *dims;
+  const Layout L = layout(d, quant_flags, 0);
+  if (L.total > 0 && (!workspace || workspace_bytes < L.total || !aligned16(workspace))) return QAT_EWORKSPACE;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const qat::Shape s = shape_of(d);
+  const void *qa = q, *ka = k, *va = v;
+  if (quant_flags & QAT_QKV_QUANT) {
+    char* ws = static_cast<char*>(workspace);
+    const long BH = (long)d.B * d.H;
+    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nq, q, ws + L.qh, st));
+    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nkv, k, ws + L.kh, st));
+    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nkv, v, ws + L.vh, st));
+    qa = ws + L.qh;
+    ka = ws + L.kh;
+    va = ws + L.vh;
+  }
+  QAT_TRY(qat::launch_fwd(s, qa, ka, va, v_scale, sm_scale, causal != 0, pfmt_of(quant_flags),
+                          (quant_flags & QAT_V_FP8_E5M2) != 0, o, o_hp, lse, st));
+  return QAT_OK;
+}
+
+int qat_attn_bwd(const qat_attn_dims* dims, const void* q, const void* k, const void* v,
+                 const float* v_scale, const void* o_hp, const float* lse, const void* dout,
+                 float sm_scale, int causal, uint32_t quant_flags,
+                 void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  bool empty = false;
+  int rc = check_common(dims, sm_scale, causal, quant_flags, v_scale, &empty);
+  if (rc != QAT_OK) return rc;
+  if (empty) return QAT_OK;
+  const void* need[] = {q, k, v, o_hp, lse, dout, dq, dk, dv};
+  for (const void* p : need)
+    if ((rc = check_ptr(p)) != QAT_OK) return rc;
+  if (v_scale && !aligned16(v_scale)) return QAT_EINVAL;
+  const qat_attn_dims& d = *dims;
+  const Layout L = layout(d, quant_flags, 1);
+  if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return QAT_EWORKSPACE;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const qat::Shape s = shape_of(d);
+  char* ws = static_cast<char*>(workspace);
+  const void *qa = q, *ka = k, *va = v;
+  if (quant_flags & QAT_QKV_QUANT) {
+    const long BH = (long)d.B * d.H;
+    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nq, q, ws + L.qh, st));
+    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nkv, k, ws + L.kh, st));
+    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nkv, v, ws + L.vh, st));
+    qa = ws + L.qh;
+    ka = ws + L.kh;
+    va = ws + L.vh;
+  }
+  float* delta = reinterpret_cast<float*>(ws + L.delta);
+  float* amax = (quant_flags & QAT_P_QUANT) ? reinterpret_cast<float*>(ws + L.amax) : nullptr;
+  const int pfmt = pfmt_of(quant_flags);
+  const bool vfp8 = (quant_flags & QAT_V_FP8_E5M2) != 0;
+  QAT_TRY(qat::launch_bwd_delta(s, o_hp, dout, delta, st));
+  QAT_TRY(qat::launch_bwd_dq(s, qa, ka, va, v_scale, dout, lse, delta, sm_scale, causal != 0, pfmt, vfp8,
+                             dq, amax, st));
+  QAT_TRY(qat::launch_bwd_dkdv(s, qa, ka, va, v_scale, dout, lse, delta, amax, sm_scale, causal != 0, pfmt,
+                               vfp8, dk, dv, st));
+  return QAT_OK;
+}
+
+int qat_quant_v_fp8(const qat_attn_dims* dims, const void* v, uint8_t* codes, float* v_scale,
+                    void* stream) {
+  if (!dims) return QAT_EINVAL;
+  const qat_attn_dims& d = *dims;
+  if (d.B < 0 || d.H < 0 || d.Nkv < 0 || d.D <= 0) return QAT_EINVAL;
+  if (d.dtype != QAT_DTYPE_BF16 && d.dtype != QAT_DTYPE_FP16) return QAT_EINVAL;
+  if (d.D != 64 && d.D != 128) return QAT_EUNSUPPORTED;
+  if ((long long)d.B * d.H > 0x7fffffff) return QAT_EUNSUPPORTED;
+  if ((long long)d.B * d.H * d.Nkv == 0) return QAT_OK;
+  if (!v || !codes || !v_scale || !aligned16(v) || !aligned16(codes) || !aligned16(v_scale)) return QAT_EINVAL;
+  QAT_TRY(qat::launch_v_quant(d.dtype, d.D, d.B * d.H, d.Nkv, v, codes, v_scale,
+                              static_cast<hipStream_t>(stream)));
+  return QAT_OK;
+}
+
+int qat_fake_quant_rows(const float* x, int32_t rows, int32_t cols, int32_t group, int32_t fmt,
+                        uint8_t* codes, float* scales, float* xhat, void* stream) {
+  if (!x || rows <= 0 || cols <= 0 || group <= 0 || (fmt != 0 && fmt != 1)) return QAT_EINVAL;
+  QAT_TRY(qat::launch_fq_rows(x, rows, cols, group, fmt, codes, scales, xhat,
+                              static_cast<hipStream_t>(stream)));
+  return QAT_OK;
+}
+
+int qat_attn_p_group(void) { return QAT_ATTN_P_GROUP; }
+
+const char* qat_attn_strerror(int status) {
+  switch (status) {
+    case QAT_OK: return "ok";
+    case QAT_EINVAL: return "invalid argument";
+    case QAT_EUNSUPPORTED: return "unsupported configuration";
+    case QAT_EWORKSPACE: return "workspace missing or too small";
+    case QAT_EHIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

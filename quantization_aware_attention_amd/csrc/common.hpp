@@ -1,0 +1,178 @@
+// Shared device helpers for the gfx950 quantization-aware attention kernels:
+// vector types, MFMA wrappers, the LDS tile swizzle, the transposing LDS read,
+// dtype packing and the fake quantizer FQ.
+//
+// MFMA operand layouts used throughout (v_mfma_f32_32x32x16_{bf16,f16}),
+// lane l in 0..63, g = l / 32:
+//   A[m][k]: lane holds m = l % 32, k = 8g + j (j = 0..7, one 16-byte operand)
+//   B[k][n]: lane holds n = l % 32, k = 8g + j
+//   C[m][n]: lane holds n = l % 32, m = 8(r/4) + 4g + r%4 (r = 0..15)
+// An accumulator block therefore gives each lane one column n and 16 rows m;
+// the 16 rows of registers 8h..8h+7 (h = 0, 1) are the rows
+// 16h + 8(j/4) + 4g + j%4, which is exactly the k order a 16-deep operand
+// needs when those registers are reused as an A or B operand ("permuted k").
+// Tiles read from LDS as the other operand follow the same permuted k order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qat {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int P_GROUP = 64;          // key columns per P-quant scale
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- dtypes
+struct BF16 {
+  typedef __bf16 scalar;
+  typedef bf16x8 vec8;
+  __device__ static inline f32x16 mfma(const s16x8& a, const s16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16((bf16x8)a, (bf16x8)b, c, 0, 0, 0);
+  }
+  // two fp32 -> packed pair (round to nearest even)
+  __device__ static inline uint32_t pack2(float x, float y) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 v = {(__bf16)x, (__bf16)y};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static inline float to_f32(uint16_t bits) {
+    return __builtin_bit_cast(float, (uint32_t)bits << 16);
+  }
+};
+
+struct FP16 {
+  typedef _Float16 scalar;
+  typedef f16x8 vec8;
+  __device__ static inline f32x16 mfma(const s16x8& a, const s16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16((f16x8)a, (f16x8)b, c, 0, 0, 0);
+  }
+  __device__ static inline uint32_t pack2(float x, float y) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    f16x2 v = {(_Float16)x, (_Float16)y};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static inline float to_f32(uint16_t bits) {
+    return (float)__builtin_bit_cast(_Float16, bits);
+  }
+};
+
+// ---------------------------------------------------------------- LDS tiles
+// A tile of R rows x D 16-bit elements lives in LDS as rows of D*2 bytes,
+// split into 16-byte chunks; chunk c of row R is stored at chunk position
+// c ^ swz(R).  With D = 128 this makes both access patterns conflict-free:
+//  * 16 consecutive rows, one chunk each (row-major operand reads), and
+//  * 4 consecutive rows x 4 consecutive chunks (transposing reads).
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (row >> 1) & 7;
+}
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int chunk) {  // byte offset
+  return row * (D * 2) + ((chunk ^ swz<D>(row)) << 4);
+}
+
+// Row-major operand: 8 consecutive elements (one chunk) of `row`.
+template <int D>
+__device__ __forceinline__ s16x8 lds_row8(const char* tile, int row, int chunk) {
+  return *reinterpret_cast<const s16x8*>(tile + tile_off<D>(row, chunk));
+}
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposed operand for a 16-deep k step: lane l receives the elements
+// (row0 + 8(j/4) + 4g + j%4, col0 + l%32) for j = 0..7, i.e. one column of
+// the tile over the permuted k order, from two ds_read_b64_tr_b16.
+// Within each 16-lane group the instruction hands lane i, slot s, element
+// i%4 of the 8 bytes read by lane 4s + i/4; so lane (4s + q) of the group
+// reads row (base + s), columns col0 + 16*(group%2) + 4q .. +3.
+template <int D>
+__device__ __forceinline__ s16x8 lds_tr8(const char* tile, int row0, int col0, int lane) {
+  const int G = lane >> 4, i = lane & 15, g = lane >> 5;
+  const int row = row0 + 4 * g + (i >> 2);
+  const int col = col0 + 16 * (G & 1) + 4 * (i & 3);
+  const int chunk = col >> 3, within = (col & 7) * 2;
+  const char* p0 = tile + tile_off<D>(row, chunk) + within;
+  const char* p1 = tile + tile_off<D>(row + 8, chunk) + within;
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
+  return (s16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// ---------------------------------------------------------------- FQ
+// One group's scale pair: s = fp32(a/FMAX), r = fp32(FMAX/a), both correctly
+// rounded divisions; a == 0 or an r that overflows gives s = r = 0 (the group
+// quantizes to zeros).
+struct FqScale { float s, r; };
+
+__device__ __forceinline__ FqScale fq_scale(float a, float fmax) {
+  float r = fmax / a;
+  float s = a / fmax;
+  const bool ok = (a > 0.0f) && (r <= 3.402823466e38f);
+  FqScale q;
+  q.s = ok ? s : 0.0f;
+  q.r = ok ? r : 0.0f;
+  return q;
+}
+
+// FMT: 0 = e4m3fn (FMAX 448), 1 = e5m2 (FMAX 57344)
+template <int FMT> struct Fp8Fmt;
+template <> struct Fp8Fmt<0> {
+  static constexpr float FMAX = 448.0f;
+  __device__ static inline uint32_t cvt2(float a, float b) {   // RNE onto the e4m3 grid
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+  }
+  __device__ static inline f32x2 val2(uint32_t pk) {
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)pk, false);
+  }
+};
+template <> struct Fp8Fmt<1> {
+  static constexpr float FMAX = 57344.0f;
+  __device__ static inline uint32_t cvt2(float a, float b) {   // RNE onto the e5m2 grid
+    return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false) & 0xFFFFu;
+  }
+  __device__ static inline f32x2 val2(uint32_t pk) {
+    return __builtin_amdgcn_cvt_pk_f32_bf8((int)pk, false);
+  }
+};
+
+// Fake-quantize a pair of values: v = fp32(x*r), code = RNE(v), x^ = fp32(code*s).
+// The two values may belong to different groups (scales q0, q1).  Returns
+// the dequantized pair; *codes gets the two 8-bit codes (low byte first).
+template <int FMT>
+__device__ __forceinline__ f32x2 fq_pair2(float x0, float x1, FqScale q0, FqScale q1,
+                                          uint32_t* codes = nullptr) {
+  const float v0 = x0 * q0.r;
+  const float v1 = x1 * q1.r;
+  const uint32_t pk = Fp8Fmt<FMT>::cvt2(v0, v1);
+  if (codes) *codes = pk;
+  const f32x2 c = Fp8Fmt<FMT>::val2(pk);
+  f32x2 out;
+  out[0] = c[0] * q0.s;
+  out[1] = c[1] * q1.s;
+  return out;
+}
+template <int FMT>
+__device__ __forceinline__ f32x2 fq_pair(float x0, float x1, FqScale q, uint32_t* codes = nullptr) {
+  return fq_pair2<FMT>(x0, x1, q, q, codes);
+}
+
+// ---------------------------------------------------------------- misc
+__device__ __forceinline__ float shfl_xor32(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace qat

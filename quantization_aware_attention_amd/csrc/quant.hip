@@ -1,0 +1,158 @@
+// Stand-alone fake-quant kernels:
+//  * per-token e4m3 fake quant of Q, K, V over the head dim (the
+//    fake_quantize_q / fake_quantize_kv pre-pass that _attention.forward in
+//    the FastVideo attn_qat_train.py source runs before the attention kernel;
+//    like that source, the fake-quantized copy keeps the input dtype);
+//  * per-channel e5m2 quantization of V to codes + scale (the fp8 V path);
+//  * FQ of fp32 rows, a test hook that runs the very device code the
+//    attention kernels use.
+// All three are HBM-bound streaming kernels.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace qat {
+
+// 16 lanes per token row of D <= 128 elements: lane handles D/16 consecutive
+// elements (8 for D = 128, 4 for D = 64).
+template <class DT, int D>
+__global__ __launch_bounds__(256) void token_quant_kernel(const uint16_t* __restrict__ x,
+                                                          uint16_t* __restrict__ xhat, long rows) {
+  constexpr int EPL = D / 16;   // elements per lane
+  const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  const bool valid = row < rows;
+  float v[EPL];
+  const uint16_t* src = x + (valid ? row : 0) * D + sub * EPL;
+  if constexpr (EPL == 8) {
+    const u32x4 w = valid ? *reinterpret_cast<const u32x4*>(src) : (u32x4){0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = DT::to_f32((uint16_t)(w[e >> 1] >> (16 * (e & 1))));
+  } else {
+    const u32x2 w = valid ? *reinterpret_cast<const u32x2*>(src) : (u32x2){0, 0};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = DT::to_f32((uint16_t)(w[e >> 1] >> (16 * (e & 1))));
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(v[e]));
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+  const FqScale fs = fq_scale(amax, Fp8Fmt<0>::FMAX);
+  uint32_t outw[EPL / 2];
+#pragma unroll
+  for (int e = 0; e < EPL; e += 2) {
+    f32x2 xq = fq_pair<0>(v[e], v[e + 1], fs);
+    if (fs.r == 0.0f) xq = (f32x2){0.0f, 0.0f};   // zero group: +0, not -0
+    outw[e / 2] = DT::pack2(xq[0], xq[1]);
+  }
+  if (!valid) return;
+  uint16_t* dst = xhat + row * D + sub * EPL;
+  if constexpr (EPL == 8) *reinterpret_cast<u32x4*>(dst) = (u32x4){outw[0], outw[1], outw[2], outw[3]};
+  else *reinterpret_cast<u32x2*>(dst) = (u32x2){outw[0], outw[1]};
+}
+
+hipError_t launch_token_quant(int dtype, int D, long rows, const void* x, void* xhat, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  dim3 grid((unsigned)((rows + 15) / 16));
+  const uint16_t* xi = (const uint16_t*)x;
+  uint16_t* xo = (uint16_t*)xhat;
+  if (dtype == 0) {
+    if (D == 128) hipLaunchKernelGGL((token_quant_kernel<BF16, 128>), grid, dim3(256), 0, st, xi, xo, rows);
+    else hipLaunchKernelGGL((token_quant_kernel<BF16, 64>), grid, dim3(256), 0, st, xi, xo, rows);
+  } else {
+    if (D == 128) hipLaunchKernelGGL((token_quant_kernel<FP16, 128>), grid, dim3(256), 0, st, xi, xo, rows);
+    else hipLaunchKernelGGL((token_quant_kernel<FP16, 64>), grid, dim3(256), 0, st, xi, xo, rows);
+  }
+  return hipGetLastError();
+}
+
+// One workgroup per (b, h): thread t owns channel d = t % D and walks the
+// token rows t / D, t / D + 256 / D, ...; the column maxima are combined in
+// LDS, then every element is encoded.
+template <class DT, int D>
+__global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict__ v, uint8_t* __restrict__ codes,
+                                                      float* __restrict__ v_scale, int N) {
+  constexpr int RPS = 256 / D;   // row phases
+  __shared__ float part[RPS][D];
+  __shared__ float scale_s[D], scale_r[D];
+  const int bh = blockIdx.x;
+  const int d = threadIdx.x % D, ph = threadIdx.x / D;
+  const uint16_t* src = v + (size_t)bh * N * D;
+  float amax = 0.0f;
+  for (int n = ph; n < N; n += RPS) amax = fmaxf(amax, fabsf(DT::to_f32(src[(size_t)n * D + d])));
+  part[ph][d] = amax;
+  __syncthreads();
+  if (ph == 0) {
+    float m = part[0][d];
+#pragma unroll
+    for (int p = 1; p < RPS; ++p) m = fmaxf(m, part[p][d]);
+    const FqScale fs = fq_scale(m, Fp8Fmt<1>::FMAX);
+    scale_s[d] = fs.s;
+    scale_r[d] = fs.r;
+    v_scale[(size_t)bh * D + d] = fs.s;
+  }
+  __syncthreads();
+  const FqScale fs = {scale_s[d], scale_r[d]};
+  uint8_t* dst = codes + (size_t)bh * N * D;
+  for (int n = ph; n < N; n += RPS) {
+    uint32_t pk;
+    fq_pair<1>(DT::to_f32(src[(size_t)n * D + d]), 0.0f, fs, &pk);
+    dst[(size_t)n * D + d] = (fs.r == 0.0f) ? 0 : (uint8_t)(pk & 0xFF);
+  }
+}
+
+hipError_t launch_v_quant(int dtype, int D, int BH, int N, const void* v, uint8_t* codes,
+                          float* v_scale, hipStream_t st) {
+  if (BH <= 0) return hipSuccess;
+  const uint16_t* vi = (const uint16_t*)v;
+  if (dtype == 0) {
+    if (D == 128) hipLaunchKernelGGL((v_quant_kernel<BF16, 128>), dim3(BH), dim3(256), 0, st, vi, codes, v_scale, N);
+    else hipLaunchKernelGGL((v_quant_kernel<BF16, 64>), dim3(BH), dim3(256), 0, st, vi, codes, v_scale, N);
+  } else {
+    if (D == 128) hipLaunchKernelGGL((v_quant_kernel<FP16, 128>), dim3(BH), dim3(256), 0, st, vi, codes, v_scale, N);
+    else hipLaunchKernelGGL((v_quant_kernel<FP16, 64>), dim3(BH), dim3(256), 0, st, vi, codes, v_scale, N);
+  }
+  return hipGetLastError();
+}
+
+// Test hook: one thread per (row, group).
+template <int FMT>
+__global__ __launch_bounds__(256) void fq_rows_kernel(const float* __restrict__ x, int rows, int cols, int group,
+                                                      uint8_t* codes, float* scales, float* xhat) {
+  const int ng = (cols + group - 1) / group;
+  const long id = (long)blockIdx.x * 256 + threadIdx.x;
+  if (id >= (long)rows * ng) return;
+  const int row = (int)(id / ng), gi = (int)(id % ng);
+  const int c0 = gi * group, c1 = min(cols, c0 + group);
+  const float* src = x + (size_t)row * cols;
+  float amax = 0.0f;
+  for (int c = c0; c < c1; ++c) amax = fmaxf(amax, fabsf(src[c]));
+  const FqScale fs = fq_scale(amax, Fp8Fmt<FMT>::FMAX);
+  if (scales) scales[(size_t)row * ng + gi] = fs.s;
+  const bool zero = fs.r == 0.0f;
+  for (int c = c0; c < c1; c += 2) {
+    const bool two = c + 1 < c1;
+    uint32_t pk;
+    const f32x2 xq = fq_pair<FMT>(src[c], two ? src[c + 1] : 0.0f, fs, &pk);
+    if (codes) {
+      codes[(size_t)row * cols + c] = zero ? 0 : (uint8_t)(pk & 0xFF);
+      if (two) codes[(size_t)row * cols + c + 1] = zero ? 0 : (uint8_t)((pk >> 8) & 0xFF);
+    }
+    if (xhat) {
+      xhat[(size_t)row * cols + c] = zero ? 0.0f : xq[0];
+      if (two) xhat[(size_t)row * cols + c + 1] = zero ? 0.0f : xq[1];
+    }
+  }
+}
+
+hipError_t launch_fq_rows(const float* x, int rows, int cols, int group, int fmt, uint8_t* codes,
+                          float* scales, float* xhat, hipStream_t st) {
+  const long n = (long)rows * ((cols + group - 1) / group);
+  if (n <= 0) return hipSuccess;
+  dim3 grid((unsigned)((n + 255) / 256));
+  if (fmt == 0) hipLaunchKernelGGL((fq_rows_kernel<0>), grid, dim3(256), 0, st, x, rows, cols, group, codes, scales, xhat);
+  else hipLaunchKernelGGL((fq_rows_kernel<1>), grid, dim3(256), 0, st, x, rows, cols, group, codes, scales, xhat);
+  return hipGetLastError();
+}
+
+}  // namespace qat

@@ -1,0 +1,186 @@
+"""ctypes binding of libqat_attn.so (C ABI in include/qat_attn.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library.  torch provides device memory and the current stream.
+The binding raises when the library is missing; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqat_attn.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "qat_attn.h")
+
+# status codes and flags (values of include/qat_attn.h)
+QAT_OK, QAT_EINVAL, QAT_EUNSUPPORTED, QAT_EWORKSPACE, QAT_EHIP = 0, 1, 2, 3, 4
+QAT_DTYPE_BF16, QAT_DTYPE_FP16 = 0, 1
+QAT_P_QUANT = 1 << 0
+QAT_P_E5M2 = 1 << 1
+QAT_QKV_QUANT = 1 << 2
+QAT_V_FP8_E5M2 = 1 << 3
+
+_DTYPES = {torch.bfloat16: QAT_DTYPE_BF16, torch.float16: QAT_DTYPE_FP16}
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Nq", ctypes.c_int32),
+                ("Nkv", ctypes.c_int32), ("D", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class QatError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def header_functions():
+    """Names of the functions include/qat_attn.h declares."""
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(qat_[a-z0-9_]+)\s*\(", txt)))
+
+
+def lib():
+    """Load libqat_attn.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32, u32, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float
+    dp = ctypes.POINTER(Dims)
+    L.qat_attn_fwd.argtypes = [dp, vp, vp, vp, vp, f32, ctypes.c_int, u32, vp, vp, vp, vp, sz, vp]
+    L.qat_attn_fwd.restype = ctypes.c_int
+    L.qat_attn_bwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, f32, ctypes.c_int, u32, vp, vp, vp, vp, sz, vp]
+    L.qat_attn_bwd.restype = ctypes.c_int
+    L.qat_attn_workspace_bytes.argtypes = [dp, u32, ctypes.c_int]
+    L.qat_attn_workspace_bytes.restype = sz
+    L.qat_quant_v_fp8.argtypes = [dp, vp, vp, vp, vp]
+    L.qat_quant_v_fp8.restype = ctypes.c_int
+    L.qat_fake_quant_rows.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp]
+    L.qat_fake_quant_rows.restype = ctypes.c_int
+    L.qat_attn_p_group.argtypes = []
+    L.qat_attn_p_group.restype = ctypes.c_int
+    L.qat_attn_strerror.argtypes = [ctypes.c_int]
+    L.qat_attn_strerror.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(fn, status):
+    if status != QAT_OK:
+        raise QatError(fn, status, lib().qat_attn_strerror(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, dtype=None):
+    if not (t.is_cuda and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous CUDA tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def dims_of(q, k):
+    B, H, Nq, D = q.shape
+    return Dims(B, H, Nq, k.shape[2], D, _DTYPES[q.dtype])
+
+
+def workspace_bytes(dims: Dims, quant_flags: int, pass_: int) -> int:
+    return int(lib().qat_attn_workspace_bytes(ctypes.byref(dims), quant_flags, pass_))
+
+
+def p_group() -> int:
+    return int(lib().qat_attn_p_group())
+
+
+def attn_fwd(q, k, v, sm_scale, causal=False, quant_flags=QAT_P_QUANT, v_scale=None,
+             out=None, workspace=None):
+    """Forward: returns (o, o_hp, lse).  With QAT_V_FP8_E5M2, ``v`` is uint8
+    e5m2 codes and ``v_scale`` fp32 [B, H, D]."""
+    _need(q, "q")
+    _need(k, "k", q.dtype)
+    _need(v, "v", torch.uint8 if quant_flags & QAT_V_FP8_E5M2 else q.dtype)
+    if v_scale is not None:
+        _need(v_scale, "v_scale", torch.float32)
+    dims = dims_of(q, k)
+    if out is None:
+        o = torch.empty_like(q)
+        o_hp = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], device=q.device, dtype=torch.float32)
+    else:
+        o, o_hp, lse = out
+    nbytes = workspace_bytes(dims, quant_flags, 0)
+    if workspace is None and nbytes:
+        workspace = torch.empty(nbytes, device=q.device, dtype=torch.uint8)
+    st = lib().qat_attn_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(v_scale),
+                            float(sm_scale), int(bool(causal)), quant_flags, _ptr(o), _ptr(o_hp),
+                            _ptr(lse), _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                            _stream())
+    _check("qat_attn_fwd", st)
+    return o, o_hp, lse
+
+
+def attn_bwd(q, k, v, o_hp, lse, dout, sm_scale, causal=False, quant_flags=QAT_P_QUANT,
+             v_scale=None, out=None, workspace=None):
+    """Straight-through backward: returns (dq, dk, dv)."""
+    _need(q, "q")
+    _need(k, "k", q.dtype)
+    _need(v, "v", torch.uint8 if quant_flags & QAT_V_FP8_E5M2 else q.dtype)
+    _need(o_hp, "o_hp", q.dtype)
+    _need(lse, "lse", torch.float32)
+    _need(dout, "dout", q.dtype)
+    dims = dims_of(q, k)
+    if out is None:
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(k)
+        dv = torch.empty(k.shape, device=k.device, dtype=q.dtype)
+    else:
+        dq, dk, dv = out
+    nbytes = workspace_bytes(dims, quant_flags, 1)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), device=q.device, dtype=torch.uint8)
+    st = lib().qat_attn_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(v_scale), _ptr(o_hp),
+                            _ptr(lse), _ptr(dout), float(sm_scale), int(bool(causal)), quant_flags,
+                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream())
+    _check("qat_attn_bwd", st)
+    return dq, dk, dv
+
+
+def quant_v_fp8(v):
+    """Per-(b, h, d) e5m2 quantization of V: returns (codes uint8, v_scale fp32 [B, H, D])."""
+    _need(v, "v")
+    B, H, N, D = v.shape
+    dims = Dims(B, H, 0, N, D, _DTYPES[v.dtype])
+    codes = torch.empty(v.shape, device=v.device, dtype=torch.uint8)
+    v_scale = torch.empty((B, H, D), device=v.device, dtype=torch.float32)
+    _check("qat_quant_v_fp8", lib().qat_quant_v_fp8(ctypes.byref(dims), _ptr(v), _ptr(codes), _ptr(v_scale), _stream()))
+    return codes, v_scale
+
+
+def fake_quant_rows(x, group, fmt):
+    """FQ of fp32 rows (fmt 0 = e4m3fn, 1 = e5m2): returns (codes, scales, xhat)."""
+    _need(x, "x", torch.float32)
+    rows, cols = x.shape
+    ng = -(-cols // group)
+    codes = torch.empty((rows, cols), device=x.device, dtype=torch.uint8)
+    scales = torch.empty((rows, ng), device=x.device, dtype=torch.float32)
+    xhat = torch.empty((rows, cols), device=x.device, dtype=torch.float32)
+    _check("qat_fake_quant_rows", lib().qat_fake_quant_rows(_ptr(x), rows, cols, group, fmt, _ptr(codes),
+                                                            _ptr(scales), _ptr(xhat), _stream()))
+    return codes, scales, xhat

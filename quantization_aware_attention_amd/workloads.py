@@ -77,8 +77,9 @@ def make_inputs(w: Workload, heads=None):
 
     Returns a dict of float32 value arrays ``q, k, v, do`` (exactly the
     dtype-rounded numbers) and uint16 storage arrays ``q_bits`` ... .  With
-    ``heads`` (an int ``n``) only the first ``n`` heads of batch 0 are drawn,
-    with the same per-head streams as the full tensor.
+    ``heads`` (an int ``n``) only the first ``n`` (b, h) heads in batch-major
+    order are drawn, as a [1, n, N, D] tensor, with the same per-head streams
+    as the full tensor.
 
     Every (b, h) head has its own PCG64 stream derived from the workload seed,
     so a head's data does not depend on how many heads are drawn.
@@ -88,18 +89,19 @@ def make_inputs(w: Workload, heads=None):
         pairs = pairs[:heads]
     B = w.B if heads is None else 1
     H = w.H if heads is None else len(pairs)
-    out = {}
     shapes = {"q": (w.Nq, w.D), "k": (w.Nkv, w.D), "v": (w.Nkv, w.D), "do": (w.Nq, w.D)}
-    bufs = {n: np.empty((B, H) + s, dtype=np.float64) for n, s in shapes.items()}
+    out = {}
+    for n, s in shapes.items():
+        out[n] = np.empty((B, H) + s, dtype=np.float32)
+        out[n + "_bits"] = np.empty((B, H) + s, dtype=np.uint16)
     offset_rng = np.random.Generator(np.random.PCG64([w.seed, 7]))
     k_off = offset_rng.standard_normal((w.H, w.D)) * np.sqrt(w.k_offset_var)
     for i, (b, h) in enumerate(pairs):
         rng = np.random.Generator(np.random.PCG64([w.seed, b, h]))
         bb, hh = (b, h) if heads is None else (0, i)
         for n in ("q", "k", "v", "do"):
-            bufs[n][bb, hh] = rng.standard_normal(shapes[n])
-        if w.k_offset_var:
-            bufs["k"][bb, hh] += k_off[h][None, :]
-    for n, x in bufs.items():
-        out[n], out[n + "_bits"] = round_to_dtype(x, w.dtype)
+            x = rng.standard_normal(shapes[n])
+            if n == "k" and w.k_offset_var:
+                x += k_off[h][None, :]
+            out[n][bb, hh], out[n + "_bits"][bb, hh] = round_to_dtype(x, w.dtype)
     return out

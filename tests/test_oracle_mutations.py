@@ -53,13 +53,15 @@ def _pins_fp8():
 
 MUTANTS = [
     # (module, function, original snippet, mutated snippet, pin family)
-    (qa_mod, "backward_head", "float(sm_scale) * (dS[:, k_rows].T @ qh[r])", "(dS[:, k_rows].T @ qh[r])", "attn"),
-    (qa_mod, "backward_head", "float(sm_scale) * (dS[sel] @ kh)", "(dS[sel] @ kh)", "attn"),
-    (qa_mod, "backward_head", "Delta = np.sum(do[r] * O_hp, axis=1)", "Delta = np.sum(do[r] * (Ph @ vh), axis=1)", "attn"),
-    (qa_mod, "backward_head", "dS = P * (dP - Delta[:, None])", "dS = P * (dP + Delta[:, None])", "attn"),
-    (qa_mod, "backward_head", "dS = P * (dP - Delta[:, None])", "dS = Ph * (dP - Delta[:, None])", "attn"),
+    (qa_mod, "backward_head", "float(sm_scale) * (dS.T @ qh[r])", "(dS.T @ qh[r])", "attn"),
+    (qa_mod, "backward_head", "float(sm_scale) * (dS_q @ kh)", "(dS_q @ kh)", "attn"),
+    (qa_mod, "backward_head", "Delta = np.sum(do[r] * O_hp, axis=1)", "Delta = np.sum(do[r] * (_p_hat(P, p_quant, p_fmt, group) @ vh), axis=1)", "attn"),
+    (qa_mod, "backward_head", "dS = P[:, k_rows] * (dP - Delta[:, None])", "dS = P[:, k_rows] * (dP + Delta[:, None])", "attn"),
+    (qa_mod, "backward_head", "dS_q = P[sel] * (dP_q - Delta[sel, None])", "dS_q = P[sel] * dP_q", "attn"),
+    (qa_mod, "backward_head", "dS = P[:, k_rows] * (dP - Delta[:, None])", "dS = Ph[:, k_rows] * (dP - Delta[:, None])", "attn"),
     (qa_mod, "backward_head", "dV += Ph[:, k_rows].T @ do[r]", "dV += P[:, k_rows].T @ do[r]", "attn"),
-    (qa_mod, "backward_head", "dP = do[r] @ vh.T", "dP = do[r] @ vh[::-1].T", "attn"),
+    (qa_mod, "backward_head", "dP = do[r] @ vh[k_rows].T", "dP = do[r] @ vh[k_rows][::-1].T", "attn"),
+    (qa_mod, "backward_head", "c = slice(g * group, min(Nkv, (g + 1) * group))", "c = slice(g * group + 1, min(Nkv, (g + 1) * group))", "attn"),
     (qa_mod, "_scores", "cols[None, :] > rows[:, None]", "cols[None, :] > rows[:, None] + 1", "attn"),
     (qa_mod, "_scores", "float(sm_scale) * (qh[rows] @ kh.T)", "(qh[rows] @ kh.T)", "attn"),
     (qa_mod, "_softmax_rows", "lse = m[:, 0] + np.log(", "lse = m[:, 0] + np.log2(", "attn"),
