@@ -1,0 +1,184 @@
+#!/usr/bin/env python3
+"""Benchmark of quantization-aware attention (forward + straight-through
+backward) on one MI355X.
+
+A step is one pass of the whole hot path over the DiT image joint-attention
+batch (B1 H24 N4608 D128 bf16, P fake-quant e4m3): the forward (scores,
+online softmax, P fake quant, O and O_hp, log-sum-exp) and the backward
+(Delta, dQ, dK/dV).  Inputs are seeded synthetic tensors already resident in
+HBM; outputs and workspaces are allocated once, outside the timed region.
+
+Prints one JSON line (rank 0):
+  value     credited TFLOP/s: 16 W / step time, W = B H Nq Nkv D
+            (forward: QK^T, P^V, P_hp V; backward: S, dP, dV, dQ, dK;
+            recomputation in the split backward is not credited)
+  roofline  the slowest kernel of the step, timed with HIP events on the
+            stream it runs on, against the bf16 dense MFMA peak
+  cpu_baseline  the float64 oracle on a bounded sample (two heads) on the
+            host cores, scaled to TFLOP/s
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "QAT attn fwd+bwd TFLOP/s, B1 H24 N4608 D128 bf16; % of MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dit_image")
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the oracle sample (0: skip)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the kernel runs on one "
+              "GPU's share of the heads); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from quantization_aware_attention_amd import ops
+    from quantization_aware_attention_amd import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[w.dtype]
+
+    inp = W.make_inputs(w)
+    def up(name):
+        return torch.from_numpy(inp[name + "_bits"].view(np.int16)).view(tdt).to(dev)
+    q, k, v, do = up("q"), up("k"), up("v"), up("do")
+    flags = ops.QAT_P_QUANT | (ops.QAT_P_E5M2 if w.p_fmt == "e5m2" else 0)
+    flags |= ops.QAT_QKV_QUANT if w.qkv_quant else 0
+    v_scale = None
+    if w.v_fp8:
+        flags |= ops.QAT_V_FP8_E5M2
+        v, v_scale = ops.quant_v_fp8(v)
+    dims = ops.dims_of(q, k)
+    o, o_hp = torch.empty_like(q), torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], device=dev, dtype=torch.float32)
+    dq, dk = torch.empty_like(q), torch.empty_like(k)
+    dv = torch.empty(k.shape, device=dev, dtype=tdt)
+    ws_f = torch.empty(max(256, ops.workspace_bytes(dims, flags, 0)), device=dev, dtype=torch.uint8)
+    ws_b = torch.empty(max(256, ops.workspace_bytes(dims, flags, 1)), device=dev, dtype=torch.uint8)
+
+    def fwd():
+        ops.attn_fwd(q, k, v, w.sm_scale, w.causal, flags, v_scale=v_scale, out=(o, o_hp, lse), workspace=ws_f)
+
+    def bwd(stages=ops.QAT_BWD_ALL):
+        ops.attn_bwd(q, k, v, o_hp, lse, do, w.sm_scale, w.causal, flags, v_scale=v_scale,
+                     out=(dq, dk, dv), workspace=ws_b, stages=stages)
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+
+    Wn = w.B * w.H * w.Nq * w.Nkv * w.D
+    if w.causal:
+        Wn = Wn * (w.Nq + 1) / (2 * w.Nq)
+    credited = 16.0 * Wn
+    value = credited / (ms_step * 1e-3) / 1e12
+
+    # ---- per-kernel durations (each call below launches exactly one kernel)
+    kernels = {
+        "fwd_kernel": (fwd, 6.0 * Wn),
+        "delta_kernel": (lambda: bwd(ops.QAT_BWD_DELTA), None),
+        "dq_kernel": (lambda: bwd(ops.QAT_BWD_DQ), 2.0 * Wn),
+        "dkdv_kernel": (lambda: bwd(ops.QAT_BWD_DKDV), 8.0 * Wn),
+    }
+    if w.qkv_quant:
+        kernels = {n: kv for n, kv in kernels.items() if n != "fwd_kernel"}
+    kernel_ms = {}
+    for name, (fn, _) in kernels.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.kernel_reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        kernel_ms[name] = e0.elapsed_time(e1) / args.kernel_reps
+    dom = max((n for n in kernels if kernels[n][1] is not None), key=lambda n: kernel_ms[n])
+    dom_tflops = kernels[dom][1] / (kernel_ms[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(dom_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": dom,
+                "kernel_ms": {n: round(t, 4) for n, t in kernel_ms.items()}}
+
+    # ---- float64 oracle on a bounded sample of the same workload
+    cpu = None
+    if args.cpu_heads > 0:
+        from threadpoolctl import threadpool_info
+
+        from oracle import qat_attention as oracle
+        nh = min(args.cpu_heads, w.B * w.H)
+        sample = W.make_inputs(w, heads=nh)
+        v_codes = vs = None
+        if w.v_fp8:
+            v_codes, vs = oracle.quantize_v_channels(sample["v"], "e5m2")
+        c0 = time.perf_counter()
+        kw = dict(causal=w.causal, p_fmt=w.p_fmt, qkv_quant=w.qkv_quant, v_codes=v_codes, v_scale=vs)
+        oracle.attention_forward(sample["q"], sample["k"], sample["v"], w.sm_scale, **kw)
+        oracle.attention_backward(sample["q"], sample["k"], sample["v"], sample["do"], w.sm_scale, **kw)
+        c1 = time.perf_counter()
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        cpu = {"value": round(credited / (w.B * w.H) * nh / (c1 - c0) / 1e12, 6), "unit": "TFLOP/s",
+               "cores": threads, "kind": "oracle",
+               "sample": f"{nh} of {w.B * w.H} heads, forward + backward, float64 NumPy, {c1 - c0:.1f} s"}
+
+    fa_conv = 14.0 * Wn / (ms_step * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B{w.B} H{w.H} Nq{w.Nq} Nkv{w.Nkv} D{w.D} {w.dtype}, "
+                               f"{'causal' if w.causal else 'non-causal'}, P fake-quant {w.p_fmt}"
+                               f"{', Q/K/V fake-quant e4m3' if w.qkv_quant else ''}"
+                               f"{', V e5m2' if w.v_fp8 else ''}",
+                   "credited_flop_per_step": credited, "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+                   "fa_convention_tflops": round(fa_conv, 2)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

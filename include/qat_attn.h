@@ -118,6 +118,32 @@ int qat_attn_bwd(const qat_attn_dims* dims, const void* q, const void* k, const 
                  void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                  void* stream);
 
+/*
+ * The backward as separately launchable stages, for callers that time,
+ * interleave or overlap them.  Arguments and workspace are those of
+ * qat_attn_bwd; `stages` is a mask of
+ *   QAT_BWD_PREPARE  Q/K/V fake quant into the workspace (QAT_QKV_QUANT only)
+ *   QAT_BWD_DELTA    Delta = rowsum(dout o o_hp) into the workspace
+ *   QAT_BWD_DQ       dq, and the per-(row, 64-key group) P absmax into the
+ *                    workspace (QAT_P_QUANT)
+ *   QAT_BWD_DKDV     dk, dv (reads Delta and the P absmax)
+ * A stage reads what earlier stages left in the same workspace: run them in
+ * this order, on one stream, with unchanged arguments.  qat_attn_bwd is
+ * QAT_BWD_ALL.  Errors as for qat_attn_bwd; QAT_EINVAL for an empty or
+ * unknown mask.
+ */
+#define QAT_BWD_PREPARE (1u << 0)
+#define QAT_BWD_DELTA   (1u << 1)
+#define QAT_BWD_DQ      (1u << 2)
+#define QAT_BWD_DKDV    (1u << 3)
+#define QAT_BWD_ALL     (QAT_BWD_PREPARE | QAT_BWD_DELTA | QAT_BWD_DQ | QAT_BWD_DKDV)
+
+int qat_attn_bwd_stages(const qat_attn_dims* dims, const void* q, const void* k, const void* v,
+                        const float* v_scale, const void* o_hp, const float* lse, const void* dout,
+                        float sm_scale, int causal, uint32_t quant_flags,
+                        void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                        uint32_t stages, void* stream);
+
 /* Workspace bytes needed by the forward (pass 0) or the backward (pass 1);
  * 0 for invalid dims. */
 size_t qat_attn_workspace_bytes(const qat_attn_dims* dims, uint32_t quant_flags, int pass);

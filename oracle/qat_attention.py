@@ -248,22 +248,37 @@ def backward_head(qh, kh, vh, do, sm_scale, causal=False, p_quant=True, p_fmt="e
 # --------------------------------------------------------------------------
 # Whole tensors [B, H, N, D]
 # --------------------------------------------------------------------------
-def prepare_inputs(q, k, v, qkv_quant=False, v_codes=None, v_scale=None):
-    """Q^, K^, V^ as float64 arrays [B, H, N, D].
+def prepare_inputs(q, k, v, qkv_quant=False, v_codes=None, v_scale=None, heads=None):
+    """Q^, K^, V^ as float64 arrays [B, H, N, D] (only the (b, h) pairs in
+    ``heads`` are filled when given; the others stay zero).
 
     ``q``, ``k``, ``v`` hold the exact values the kernels receive (bf16 or
     fp16 values carried in a wider float type).  With ``v_codes`` given, V^ is
     the dequantized e5m2 V and ``v`` is ignored.
     """
-    qh = np.asarray(q, dtype=np.float64)
-    kh = np.asarray(k, dtype=np.float64)
+    q = np.asarray(q)
+    k = np.asarray(k)
+    B, H, Nq, D = q.shape
+    Nkv = k.shape[2]
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    qh = np.zeros((B, H, Nq, D))
+    kh = np.zeros((B, H, Nkv, D))
+    vh = np.zeros((B, H, Nkv, D))
+    for b, h in pairs:
+        qh[b, h], kh[b, h], vh[b, h] = _prepare_head(q, k, v, b, h, qkv_quant, v_codes, v_scale)
+    return qh, kh, vh
+
+
+def _prepare_head(q, k, v, b, h, qkv_quant, v_codes, v_scale):
+    qh = np.asarray(q[b, h], dtype=np.float64)
+    kh = np.asarray(k[b, h], dtype=np.float64)
     if qkv_quant:
         qh = quantize_token_rows(qh, "e4m3")[2].astype(np.float64)
         kh = quantize_token_rows(kh, "e4m3")[2].astype(np.float64)
     if v_codes is not None:
-        vh = dequant_v_channels(v_codes, v_scale, "e5m2")
+        vh = dequant_v_channels(v_codes[b:b + 1, h:h + 1], v_scale[b:b + 1, h:h + 1], "e5m2")[0, 0]
     else:
-        vh = np.asarray(v, dtype=np.float64)
+        vh = np.asarray(v[b, h], dtype=np.float64)
         if qkv_quant:
             vh = quantize_token_rows(vh, "e4m3")[2].astype(np.float64)
     return qh, kh, vh
@@ -278,15 +293,16 @@ def attention_forward(q, k, v, sm_scale, causal=False, p_quant=True, p_fmt="e4m3
     the (b, h) pairs in ``heads`` and the query ``rows`` are computed when
     given; the others stay zero / the arrays are restricted to ``rows``).
     """
-    qh, kh, vh = prepare_inputs(q, k, v, qkv_quant, v_codes, v_scale)
-    B, H, Nq, D = qh.shape
+    q = np.asarray(q)
+    B, H, Nq, D = q.shape
     nr = Nq if rows is None else len(rows)
     O = np.zeros((B, H, nr, D))
     O_hp = np.zeros_like(O)
     lse = np.zeros((B, H, nr))
     for b, h in (heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]):
+        qh, kh, vh = _prepare_head(q, k, v, b, h, qkv_quant, v_codes, v_scale)
         O[b, h], O_hp[b, h], lse[b, h] = forward_head(
-            qh[b, h], kh[b, h], vh[b, h], sm_scale, causal, p_quant, p_fmt, group, rows)
+            qh, kh, vh, sm_scale, causal, p_quant, p_fmt, group, rows)
     return O, O_hp, lse
 
 
@@ -294,18 +310,18 @@ def attention_backward(q, k, v, do, sm_scale, causal=False, p_quant=True, p_fmt=
                        qkv_quant=False, v_codes=None, v_scale=None, group=P_GROUP,
                        heads=None, q_rows=None, k_rows=None):
     """Straight-through backward over [B, H, N, D]: returns (dQ, dK, dV)."""
-    qh, kh, vh = prepare_inputs(q, k, v, qkv_quant, v_codes, v_scale)
-    B, H, Nq, D = qh.shape
-    Nkv = kh.shape[2]
+    q = np.asarray(q)
+    B, H, Nq, D = q.shape
+    Nkv = np.asarray(k).shape[2]
     nq = Nq if q_rows is None else len(q_rows)
     nk = Nkv if k_rows is None else len(k_rows)
     dQ = np.zeros((B, H, nq, D))
     dK = np.zeros((B, H, nk, D))
     dV = np.zeros((B, H, nk, D))
-    do = np.asarray(do, dtype=np.float64)
     for b, h in (heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]):
+        qh, kh, vh = _prepare_head(q, k, v, b, h, qkv_quant, v_codes, v_scale)
         dQ[b, h], dK[b, h], dV[b, h] = backward_head(
-            qh[b, h], kh[b, h], vh[b, h], do[b, h], sm_scale, causal, p_quant, p_fmt,
+            qh, kh, vh, np.asarray(do[b, h], dtype=np.float64), sm_scale, causal, p_quant, p_fmt,
             group, q_rows, k_rows)
     return dQ, dK, dV
 

@@ -20,9 +20,11 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 // Workspace layout (each piece 256-byte aligned, in this order):
 //   bwd: delta fp32 [B,H,Nq]; p_amax fp32 [B,H,ceil(Nkv/64),Nq] (P quant only)
-//   fwd and bwd: q^, k^, v^ (dtype) when Q/K/V quantization is on
+//   fwd and bwd, when Q/K/V quantization is on: the fp8 code values of Q and
+//   K (dtype) with their per-token scales (fp32 [B,H,Nq], [B,H,Nkv]), and
+//   V^ = code * scale rounded to the dtype
 struct Layout {
-  size_t delta = 0, amax = 0, qh = 0, kh = 0, vh = 0, total = 0;
+  size_t delta = 0, amax = 0, qh = 0, kh = 0, vh = 0, qs = 0, ks = 0, total = 0;
 };
 
 Layout layout(const qat_attn_dims& d, uint32_t flags, int pass) {
@@ -45,6 +47,10 @@ Layout layout(const qat_attn_dims& d, uint32_t flags, int pass) {
     off += align_up(BH * d.Nkv * d.D * 2);
     L.vh = off;
     off += align_up(BH * d.Nkv * d.D * 2);
+    L.qs = off;
+    off += align_up(BH * d.Nq * sizeof(float));
+    L.ks = off;
+    off += align_up(BH * d.Nkv * sizeof(float));
   }
   L.total = off;
   return L;
@@ -85,6 +91,24 @@ int pfmt_of(uint32_t flags) {
     if ((expr) != hipSuccess) return QAT_EHIP;         \
   } while (0)
 
+// The inputs the attention kernels read: the caller's tensors, or for Q/K/V
+// quantization the pre-pass outputs in the workspace (run here).
+int prepare_inputs(const qat_attn_dims& d, const Layout& L, uint32_t flags, const void* q, const void* k,
+                   const void* v, const float* v_scale, char* ws, hipStream_t st, qat::Inputs* in) {
+  *in = qat::Inputs{q, k, v, v_scale, nullptr, nullptr, qat::IN_PLAIN};
+  if (flags & QAT_V_FP8_E5M2) in->mode = qat::IN_VFP8;
+  if (flags & QAT_QKV_QUANT) {
+    const long BH = (long)d.B * d.H;
+    float* qs = reinterpret_cast<float*>(ws + L.qs);
+    float* ks = reinterpret_cast<float*>(ws + L.ks);
+    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nq, q, ws + L.qh, qs, st));
+    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nkv, k, ws + L.kh, ks, st));
+    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nkv, v, ws + L.vh, nullptr, st));
+    *in = qat::Inputs{ws + L.qh, ws + L.kh, ws + L.vh, nullptr, qs, ks, qat::IN_QKS};
+  }
+  return QAT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -114,27 +138,19 @@ int qat_attn_fwd(const qat_attn_dims* dims, const void* q, const void* k, const 
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const qat::Shape s = shape_of(d);
-  const void *qa = q, *ka = k, *va = v;
-  if (quant_flags & QAT_QKV_QUANT) {
-    char* ws = static_cast<char*>(workspace);
-    const long BH = (long)d.B * d.H;
-    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nq, q, ws + L.qh, st));
-    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nkv, k, ws + L.kh, st));
-    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nkv, v, ws + L.vh, st));
-    qa = ws + L.qh;
-    ka = ws + L.kh;
-    va = ws + L.vh;
-  }
-  QAT_TRY(qat::launch_fwd(s, qa, ka, va, v_scale, sm_scale, causal != 0, pfmt_of(quant_flags),
-                          (quant_flags & QAT_V_FP8_E5M2) != 0, o, o_hp, lse, st));
+  qat::Inputs in;
+  if ((rc = prepare_inputs(d, L, quant_flags, q, k, v, v_scale, static_cast<char*>(workspace), st, &in)) != QAT_OK)
+    return rc;
+  QAT_TRY(qat::launch_fwd(s, in, sm_scale, causal != 0, pfmt_of(quant_flags), o, o_hp, lse, st));
   return QAT_OK;
 }
 
-int qat_attn_bwd(const qat_attn_dims* dims, const void* q, const void* k, const void* v,
-                 const float* v_scale, const void* o_hp, const float* lse, const void* dout,
-                 float sm_scale, int causal, uint32_t quant_flags,
-                 void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                 void* stream) {
+int qat_attn_bwd_stages(const qat_attn_dims* dims, const void* q, const void* k, const void* v,
+                        const float* v_scale, const void* o_hp, const float* lse, const void* dout,
+                        float sm_scale, int causal, uint32_t quant_flags,
+                        void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                        uint32_t stages, void* stream) {
+  if (stages == 0 || (stages & ~QAT_BWD_ALL)) return QAT_EINVAL;
   bool empty = false;
   int rc = check_common(dims, sm_scale, causal, quant_flags, v_scale, &empty);
   if (rc != QAT_OK) return rc;
@@ -150,26 +166,30 @@ int qat_attn_bwd(const qat_attn_dims* dims, const void* q, const void* k, const 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const qat::Shape s = shape_of(d);
   char* ws = static_cast<char*>(workspace);
-  const void *qa = q, *ka = k, *va = v;
-  if (quant_flags & QAT_QKV_QUANT) {
-    const long BH = (long)d.B * d.H;
-    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nq, q, ws + L.qh, st));
-    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nkv, k, ws + L.kh, st));
-    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nkv, v, ws + L.vh, st));
-    qa = ws + L.qh;
-    ka = ws + L.kh;
-    va = ws + L.vh;
-  }
+  qat::Inputs in;
+  const uint32_t prep = (stages & QAT_BWD_PREPARE) ? quant_flags : (quant_flags & ~QAT_QKV_QUANT);
+  if ((rc = prepare_inputs(d, L, prep, q, k, v, v_scale, ws, st, &in)) != QAT_OK) return rc;
+  if (quant_flags & QAT_QKV_QUANT)   // later stages read the prepared inputs
+    in = qat::Inputs{ws + L.qh, ws + L.kh, ws + L.vh, nullptr, reinterpret_cast<float*>(ws + L.qs),
+                     reinterpret_cast<float*>(ws + L.ks), qat::IN_QKS};
   float* delta = reinterpret_cast<float*>(ws + L.delta);
   float* amax = (quant_flags & QAT_P_QUANT) ? reinterpret_cast<float*>(ws + L.amax) : nullptr;
   const int pfmt = pfmt_of(quant_flags);
-  const bool vfp8 = (quant_flags & QAT_V_FP8_E5M2) != 0;
-  QAT_TRY(qat::launch_bwd_delta(s, o_hp, dout, delta, st));
-  QAT_TRY(qat::launch_bwd_dq(s, qa, ka, va, v_scale, dout, lse, delta, sm_scale, causal != 0, pfmt, vfp8,
-                             dq, amax, st));
-  QAT_TRY(qat::launch_bwd_dkdv(s, qa, ka, va, v_scale, dout, lse, delta, amax, sm_scale, causal != 0, pfmt,
-                               vfp8, dk, dv, st));
+  if (stages & QAT_BWD_DELTA) QAT_TRY(qat::launch_bwd_delta(s, o_hp, dout, delta, st));
+  if (stages & QAT_BWD_DQ)
+    QAT_TRY(qat::launch_bwd_dq(s, in, dout, lse, delta, sm_scale, causal != 0, pfmt, dq, amax, st));
+  if (stages & QAT_BWD_DKDV)
+    QAT_TRY(qat::launch_bwd_dkdv(s, in, dout, lse, delta, amax, sm_scale, causal != 0, pfmt, dk, dv, st));
   return QAT_OK;
+}
+
+int qat_attn_bwd(const qat_attn_dims* dims, const void* q, const void* k, const void* v,
+                 const float* v_scale, const void* o_hp, const float* lse, const void* dout,
+                 float sm_scale, int causal, uint32_t quant_flags,
+                 void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  return qat_attn_bwd_stages(dims, q, k, v, v_scale, o_hp, lse, dout, sm_scale, causal, quant_flags, dq, dk,
+                             dv, workspace, workspace_bytes, QAT_BWD_ALL, stream);
 }
 
 int qat_quant_v_fp8(const qat_attn_dims* dims, const void* v, uint8_t* codes, float* v_scale,

@@ -80,7 +80,9 @@ struct BwdArgs {
   const void* q;
   const void* k;
   const void* v;
-  const float* v_scale;
+  const float* v_scale;   // IN_VFP8
+  const float* q_scale;   // IN_QKS
+  const float* k_scale;   // IN_QKS
   const void* dout;
   const float* lse;
   const float* delta;
@@ -129,12 +131,15 @@ __device__ __forceinline__ void stage_kv_tile(char* dst, const uint8_t* src, con
 constexpr int DQ_BM = 128;
 constexpr int DQ_BN = 64;
 
-template <class DT, int D, bool CAUSAL, int PQ, bool VFP8>
-__global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
+template <class DT, int D, bool CAUSAL, int PQ, int IN>
+__global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
+  constexpr bool VFP8 = IN == IN_VFP8;
+  constexpr bool QKS = IN == IN_QKS;
   constexpr int TILE = DQ_BN * D * 2;
   constexpr int NDB = D / 32;
   constexpr int NKS = D / 16;
   __shared__ __attribute__((aligned(16))) char smem[2][TILE];   // K, V of the current tile
+  __shared__ __attribute__((aligned(16))) float ks_s[DQ_BN];     // IN_QKS: key scales
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int bh = blockIdx.y;
@@ -157,6 +162,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   }
   const float Mi = qi < Nq ? a.lse[(size_t)bh * Nq + qi] * LOG2E : 0.0f;
   const float Di = qi < Nq ? a.delta[(size_t)bh * Nq + qi] : 0.0f;
+  float c_row = a.c;   // IN_QKS: s_q folds into the log2 scale (same rounding as dK/dV)
+  if constexpr (QKS) c_row = a.c * (qi < Nq ? a.q_scale[(size_t)bh * Nq + qi] : 1.0f);
 
   f32x16 dq_acc[NDB];
 #pragma unroll
@@ -169,6 +176,9 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
     __syncthreads();
     stage_kv_tile<DT, D, false>(smem[0], kp, nullptr, kv0, Nkv, tid);
     stage_kv_tile<DT, D, VFP8>(smem[1], vp, vsc, kv0, Nkv, tid);
+    if constexpr (QKS) {
+      if (tid < DQ_BN) ks_s[tid] = kv0 + tid < Nkv ? a.k_scale[(size_t)bh * Nkv + kv0 + tid] : 0.0f;
+    }
     __syncthreads();
     if (q0 >= Nq || (CAUSAL && kv0 > q0 + 31)) continue;
     const char* Kt = smem[0];
@@ -185,13 +195,27 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
       }
     }
     const bool need_mask = (kv0 + DQ_BN > Nkv) || (CAUSAL && kv0 + DQ_BN - 1 > q0);
+    float sk[2][16];
+    if constexpr (QKS) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const f32x4 v4 = *reinterpret_cast<const f32x4*>(&ks_s[kb * 32 + 8 * u + 4 * g]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sk[kb][4 * u + e] = v4[e];
+            s[kb][4 * u + e] *= v4[e];
+          }
+        }
+    }
     float p[2][16];
     float pmax = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x = fast_exp2(__builtin_fmaf(s[kb][r], a.c, -Mi));
+        float x = fast_exp2(__builtin_fmaf(s[kb][r], c_row, -Mi));
         if (need_mask) {
           const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
           if (key >= Nkv || (CAUSAL && key > qi)) x = 0.0f;
@@ -211,7 +235,12 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int r0 = 8 * h + 2 * jj;
-        w4[jj] = DT::pack2(p[kb][r0] * (dp[kb][r0] - Di), p[kb][r0 + 1] * (dp[kb][r0 + 1] - Di));
+        float d0 = p[kb][r0] * (dp[kb][r0] - Di), d1 = p[kb][r0 + 1] * (dp[kb][r0 + 1] - Di);
+        if constexpr (QKS) {   // dQ = sm_scale sum_j dS_ij s_k[j] code_k[j]
+          d0 *= sk[kb][r0];
+          d1 *= sk[kb][r0 + 1];
+        }
+        w4[jj] = DT::pack2(d0, d1);
       }
       const s16x8 ds_op = __builtin_bit_cast(s16x8, (u32x4){w4[0], w4[1], w4[2], w4[3]});
 #pragma unroll
@@ -239,8 +268,10 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 constexpr int DKV_BN = 128;   // keys per workgroup (two P groups)
 constexpr int DKV_BQ = 64;    // queries per staged tile
 
-template <class DT, int D, bool CAUSAL, int PQ, bool VFP8>
+template <class DT, int D, bool CAUSAL, int PQ, int IN>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
+  constexpr bool VFP8 = IN == IN_VFP8;
+  constexpr bool QKS = IN == IN_QKS;
   constexpr int TILE = DKV_BQ * D * 2;
   constexpr int NDB = D / 32;
   constexpr int NKS = D / 16;
@@ -250,6 +281,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char dot_s[TILE];
   __shared__ __attribute__((aligned(16))) float m_s[DKV_BQ];
   __shared__ __attribute__((aligned(16))) float d_s[DKV_BQ];
+  __shared__ __attribute__((aligned(16))) float sq_s[DKV_BQ];      // IN_QKS: query scales
   __shared__ __attribute__((aligned(16))) float qs_s[2][DKV_BQ];   // P-quant s per (group, query)
   __shared__ __attribute__((aligned(16))) float qr_s[2][DKV_BQ];   // P-quant r
 
@@ -294,6 +326,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     }
   }
 
+  const float sk_lane = QKS ? (kj < Nkv ? a.k_scale[(size_t)bh * Nkv + kj] : 0.0f) : 1.0f;
+
   f32x16 dk_acc[NDB], dv_acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
@@ -324,6 +358,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
       const int q = qt0 + tid;
       m_s[tid] = q < Nq ? a.lse[(size_t)bh * Nq + q] * LOG2E : 0.0f;
       d_s[tid] = q < Nq ? a.delta[(size_t)bh * Nq + q] : 0.0f;
+      if constexpr (QKS) sq_s[tid] = q < Nq ? a.q_scale[(size_t)bh * Nq + q] : 1.0f;
     } else if constexpr (PQ >= 0) {
       if (tid < 3 * DKV_BQ) {
         const int e = tid - DKV_BQ, gi = e / DKV_BQ, qq = e % DKV_BQ;
@@ -362,16 +397,22 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
           sv = *reinterpret_cast<const f32x4*>(&qs_s[mygrp][ql]);
           rv = *reinterpret_cast<const f32x4*>(&qr_s[mygrp][ql]);
         }
+        f32x4 sq4 = {1.0f, 1.0f, 1.0f, 1.0f};
+        if constexpr (QKS) sq4 = *reinterpret_cast<const f32x4*>(&sq_s[ql]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * u + e;
-          float x = fast_exp2(__builtin_fmaf(s[r], a.c, -mv[e]));
+          // S and the log2 scale are formed exactly as in the dQ kernel
+          const float sr = QKS ? s[r] * sk_lane : s[r];
+          const float cr = QKS ? a.c * sq4[e] : a.c;
+          float x = fast_exp2(__builtin_fmaf(sr, cr, -mv[e]));
           if (need_mask) {
             const int q = qt0 + ql + e;
             if (q >= Nq || kj >= Nkv || (CAUSAL && kj > q)) x = 0.0f;
           }
           p[r] = x;
           dsv[r] = x * (dp[r] - dv4[e]);
+          if constexpr (QKS) dsv[r] *= sq4[e];   // dK = sm_scale sum_i dS_ij s_q[i] code_q[i]
         }
         if constexpr (PQ >= 0) {
           // registers 4u+e hold different query rows: one (s, r) pair each
@@ -423,86 +464,86 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ dispatch
-template <template <class, int, bool, int, bool> class K, class DT, int D>
-struct Dispatch;
-
-template <class DT, int D, bool CAUSAL, int PQ, bool VFP8>
+template <class DT, int D, bool CAUSAL, int PQ, int IN>
 struct DqK {
   static void run(dim3 g, const BwdArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((dq_kernel<DT, D, CAUSAL, PQ, VFP8>), g, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((dq_kernel<DT, D, CAUSAL, PQ, IN>), g, dim3(256), 0, st, a);
   }
 };
-template <class DT, int D, bool CAUSAL, int PQ, bool VFP8>
+template <class DT, int D, bool CAUSAL, int PQ, int IN>
 struct DkvK {
   static void run(dim3 g, const BwdArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((dkdv_kernel<DT, D, CAUSAL, PQ, VFP8>), g, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((dkdv_kernel<DT, D, CAUSAL, PQ, IN>), g, dim3(256), 0, st, a);
   }
 };
 
-template <template <class, int, bool, int, bool> class K, class DT, int D, bool CAUSAL, bool VFP8>
+template <template <class, int, bool, int, int> class K, class DT, int D, bool CAUSAL, int IN>
 static void pick_pq(dim3 g, const BwdArgs& a, int pfmt, hipStream_t st) {
-  if (pfmt == 0) K<DT, D, CAUSAL, 0, VFP8>::run(g, a, st);
-  else if (pfmt == 1) K<DT, D, CAUSAL, 1, VFP8>::run(g, a, st);
-  else K<DT, D, CAUSAL, -1, VFP8>::run(g, a, st);
+  if (pfmt == 0) K<DT, D, CAUSAL, 0, IN>::run(g, a, st);
+  else if (pfmt == 1) K<DT, D, CAUSAL, 1, IN>::run(g, a, st);
+  else K<DT, D, CAUSAL, -1, IN>::run(g, a, st);
 }
 
-template <template <class, int, bool, int, bool> class K, class DT, int D>
-static void pick_rest(dim3 g, const BwdArgs& a, bool causal, int pfmt, bool v_fp8, hipStream_t st) {
-  if (v_fp8) {
-    if constexpr (__is_same(DT, BF16)) {
-      if (causal) pick_pq<K, DT, D, true, true>(g, a, pfmt, st);
-      else pick_pq<K, DT, D, false, true>(g, a, pfmt, st);
-    }
+template <template <class, int, bool, int, int> class K, class DT, int D, int IN>
+static void pick_causal(dim3 g, const BwdArgs& a, bool causal, int pfmt, hipStream_t st) {
+  if (causal) pick_pq<K, DT, D, true, IN>(g, a, pfmt, st);
+  else pick_pq<K, DT, D, false, IN>(g, a, pfmt, st);
+}
+
+template <template <class, int, bool, int, int> class K, class DT, int D>
+static void pick_rest(dim3 g, const BwdArgs& a, bool causal, int pfmt, int mode, hipStream_t st) {
+  if (mode == IN_VFP8) {
+    if constexpr (__is_same(DT, BF16)) pick_causal<K, DT, D, IN_VFP8>(g, a, causal, pfmt, st);
     return;
   }
-  if (causal) pick_pq<K, DT, D, true, false>(g, a, pfmt, st);
-  else pick_pq<K, DT, D, false, false>(g, a, pfmt, st);
+  if (mode == IN_QKS) pick_causal<K, DT, D, IN_QKS>(g, a, causal, pfmt, st);
+  else pick_causal<K, DT, D, IN_PLAIN>(g, a, causal, pfmt, st);
 }
 
-template <template <class, int, bool, int, bool> class K>
-static hipError_t pick_all(const Shape& s, dim3 g, const BwdArgs& a, bool causal, int pfmt, bool v_fp8,
+template <template <class, int, bool, int, int> class K>
+static hipError_t pick_all(const Shape& s, dim3 g, const BwdArgs& a, bool causal, int pfmt, int mode,
                            hipStream_t st) {
   if (s.dtype == 0) {
-    if (s.D == 128) pick_rest<K, BF16, 128>(g, a, causal, pfmt, v_fp8, st);
-    else pick_rest<K, BF16, 64>(g, a, causal, pfmt, v_fp8, st);
+    if (s.D == 128) pick_rest<K, BF16, 128>(g, a, causal, pfmt, mode, st);
+    else pick_rest<K, BF16, 64>(g, a, causal, pfmt, mode, st);
   } else {
-    if (s.D == 128) pick_rest<K, FP16, 128>(g, a, causal, pfmt, v_fp8, st);
-    else pick_rest<K, FP16, 64>(g, a, causal, pfmt, v_fp8, st);
+    if (s.D == 128) pick_rest<K, FP16, 128>(g, a, causal, pfmt, mode, st);
+    else pick_rest<K, FP16, 64>(g, a, causal, pfmt, mode, st);
   }
   return hipGetLastError();
 }
 
-static BwdArgs make_args(const Shape& s, const void* q, const void* k, const void* v, const float* v_scale,
-                         const void* dout, const float* lse, const float* delta, float sm_scale) {
+static BwdArgs make_args(const Shape& s, const Inputs& in, const void* dout, const float* lse,
+                         const float* delta, float sm_scale) {
   BwdArgs a = {};
-  a.q = q; a.k = k; a.v = v; a.v_scale = v_scale; a.dout = dout; a.lse = lse; a.delta = delta;
+  a.q = in.q; a.k = in.k; a.v = in.v;
+  a.v_scale = in.v_scale; a.q_scale = in.q_scale; a.k_scale = in.k_scale;
+  a.dout = dout; a.lse = lse; a.delta = delta;
   a.Nq = s.Nq; a.Nkv = s.Nkv; a.NG = (s.Nkv + P_GROUP - 1) / P_GROUP;
   a.sm_scale = sm_scale;
   a.c = sm_scale * LOG2E;
   return a;
 }
 
-hipError_t launch_bwd_dq(const Shape& s, const void* q, const void* k, const void* v,
-                         const float* v_scale, const void* dout, const float* lse,
-                         const float* delta, float sm_scale, bool causal, int pfmt, bool v_fp8,
+hipError_t launch_bwd_dq(const Shape& s, const Inputs& in, const void* dout, const float* lse,
+                         const float* delta, float sm_scale, bool causal, int pfmt,
                          void* dq, float* p_amax, hipStream_t st) {
-  BwdArgs a = make_args(s, q, k, v, v_scale, dout, lse, delta, sm_scale);
+  BwdArgs a = make_args(s, in, dout, lse, delta, sm_scale);
   a.dq = dq;
   a.p_amax = p_amax;
   dim3 grid((s.Nq + DQ_BM - 1) / DQ_BM, s.B * s.H);
-  return pick_all<DqK>(s, grid, a, causal, pfmt, v_fp8, st);
+  return pick_all<DqK>(s, grid, a, causal, pfmt, in.mode, st);
 }
 
-hipError_t launch_bwd_dkdv(const Shape& s, const void* q, const void* k, const void* v,
-                           const float* v_scale, const void* dout, const float* lse,
+hipError_t launch_bwd_dkdv(const Shape& s, const Inputs& in, const void* dout, const float* lse,
                            const float* delta, const float* p_amax, float sm_scale, bool causal,
-                           int pfmt, bool v_fp8, void* dk, void* dv, hipStream_t st) {
-  BwdArgs a = make_args(s, q, k, v, v_scale, dout, lse, delta, sm_scale);
+                           int pfmt, void* dk, void* dv, hipStream_t st) {
+  BwdArgs a = make_args(s, in, dout, lse, delta, sm_scale);
   a.p_amax_in = p_amax;
   a.dk = dk;
   a.dv = dv;
   dim3 grid((s.Nkv + DKV_BN - 1) / DKV_BN, s.B * s.H);
-  return pick_all<DkvK>(s, grid, a, causal, pfmt, v_fp8, st);
+  return pick_all<DkvK>(s, grid, a, causal, pfmt, in.mode, st);
 }
 
 }  // namespace qat

@@ -31,7 +31,9 @@ struct FwdArgs {
   const void* q;
   const void* k;
   const void* v;
-  const float* v_scale;
+  const float* v_scale;   // IN_VFP8: [BH, D]
+  const float* q_scale;   // IN_QKS: [BH, Nq]
+  const float* k_scale;   // IN_QKS: [BH, Nkv]
   void* o;
   void* o_hp;
   float* lse;
@@ -43,14 +45,17 @@ constexpr int FWD_BM = 128;      // query rows per workgroup
 constexpr int FWD_BN = 64;       // keys per tile (= P_GROUP)
 constexpr float RESCALE_SLACK = 8.0f;
 
-template <class DT, int D, bool CAUSAL, int PQ, bool VFP8>
+template <class DT, int D, bool CAUSAL, int PQ, int IN>
 __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
+  constexpr bool VFP8 = IN == IN_VFP8;
+  constexpr bool QKS = IN == IN_QKS;
   constexpr int CH = D / 8;                 // 16-byte chunks per row
   constexpr int TILE = FWD_BN * D * 2;      // bytes per K or V tile
   constexpr int LPT = FWD_BN * CH / 256;    // chunks per thread per tile
   constexpr int NDB = D / 32;               // 32-wide d blocks
   constexpr int NKS = D / 16;               // 16-deep k steps over D
   __shared__ __attribute__((aligned(16))) char smem[2][2][TILE];
+  __shared__ __attribute__((aligned(16))) float ks_s[2][FWD_BN];   // IN_QKS: key scales of the tile
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int bh = blockIdx.y;
@@ -70,13 +75,23 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
     else qf[ks] = (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
   }
 
+  // IN_QKS: S = s_q[i] s_k[j] (code_q . code_k); s_q folds into the log2 scale
+  float c_row = a.c;
+  if constexpr (QKS) c_row = a.c * (qi < Nq ? a.q_scale[(size_t)bh * Nq + qi] : 1.0f);
+  const float* ksp = QKS ? a.k_scale + (size_t)bh * Nkv : nullptr;
+
   const int kv_end = CAUSAL ? min(Nkv, qb + FWD_BM) : Nkv;
   const int ntiles = (kv_end + FWD_BN - 1) / FWD_BN;
 
   u32x4 kreg[LPT];
   u32x4 vreg[LPT];
   u32x2 vcode[LPT];
+  float ksreg = 0.0f;
   auto load_regs = [&](int t) {
+    if constexpr (QKS) {
+      const int key = t * FWD_BN + tid;
+      if (tid < FWD_BN) ksreg = key < Nkv ? ksp[key] : 0.0f;
+    }
 #pragma unroll
     for (int u = 0; u < LPT; ++u) {
       const int idx = tid + 256 * u, row = idx / CH, ch = idx % CH;
@@ -91,6 +106,9 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
     }
   };
   auto store_regs = [&](int buf) {
+    if constexpr (QKS) {
+      if (tid < FWD_BN) ks_s[buf][tid] = ksreg;
+    }
 #pragma unroll
     for (int u = 0; u < LPT; ++u) {
       const int idx = tid + 256 * u, row = idx / CH, ch = idx % CH;
@@ -145,6 +163,16 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
           s[kb] = DT::mfma(ka, qf[ks], s[kb]);
         }
       }
+      if constexpr (QKS) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const f32x4 sk = *reinterpret_cast<const f32x4*>(&ks_s[buf][kb * 32 + 8 * u + 4 * g]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[kb][4 * u + e] *= sk[e];
+          }
+      }
       // ---- masks: key tail, causal diagonal
       const bool need_mask = (kv0 + FWD_BN > Nkv) || (CAUSAL && kv0 + FWD_BN - 1 > q0);
       if (need_mask) {
@@ -163,7 +191,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
       mx = fmaxf(mx, shfl_xor32(mx));
-      const float t_new = mx * a.c;
+      const float t_new = mx * c_row;
       const bool resc = t_new > m_used + RESCALE_SLACK;
       if (__any(resc)) {
         const float m_new = resc ? t_new : m_used;
@@ -184,7 +212,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], a.c, -m_sub));
+          p[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c_row, -m_sub));
           psum += p[kb][r];
           pmax = fmaxf(pmax, p[kb][r]);
         }
@@ -253,48 +281,49 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
   }
 }
 
-template <class DT, int D, bool CAUSAL, int PQ, bool VFP8>
+template <class DT, int D, bool CAUSAL, int PQ, int IN>
 static hipError_t fwd_launch(const Shape& s, const FwdArgs& a, hipStream_t st) {
   dim3 grid((s.Nq + FWD_BM - 1) / FWD_BM, s.B * s.H);
-  hipLaunchKernelGGL((fwd_kernel<DT, D, CAUSAL, PQ, VFP8>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((fwd_kernel<DT, D, CAUSAL, PQ, IN>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-template <class DT, int D, bool CAUSAL, bool VFP8>
+template <class DT, int D, bool CAUSAL, int IN>
 static hipError_t fwd_pick_pq(const Shape& s, const FwdArgs& a, int pfmt, hipStream_t st) {
-  if (pfmt == 0) return fwd_launch<DT, D, CAUSAL, 0, VFP8>(s, a, st);
-  if (pfmt == 1) return fwd_launch<DT, D, CAUSAL, 1, VFP8>(s, a, st);
-  return fwd_launch<DT, D, CAUSAL, -1, VFP8>(s, a, st);
+  if (pfmt == 0) return fwd_launch<DT, D, CAUSAL, 0, IN>(s, a, st);
+  if (pfmt == 1) return fwd_launch<DT, D, CAUSAL, 1, IN>(s, a, st);
+  return fwd_launch<DT, D, CAUSAL, -1, IN>(s, a, st);
+}
+
+template <class DT, int D, int IN>
+static hipError_t fwd_pick_causal(const Shape& s, const FwdArgs& a, bool causal, int pfmt, hipStream_t st) {
+  return causal ? fwd_pick_pq<DT, D, true, IN>(s, a, pfmt, st) : fwd_pick_pq<DT, D, false, IN>(s, a, pfmt, st);
 }
 
 template <class DT, int D>
-static hipError_t fwd_pick(const Shape& s, const FwdArgs& a, bool causal, int pfmt, bool v_fp8,
-                           hipStream_t st) {
-  if (v_fp8) {
-    if constexpr (sizeof(typename DT::scalar) == 2 && __is_same(DT, BF16)) {
-      return causal ? fwd_pick_pq<DT, D, true, true>(s, a, pfmt, st)
-                    : fwd_pick_pq<DT, D, false, true>(s, a, pfmt, st);
-    }
+static hipError_t fwd_pick(const Shape& s, const FwdArgs& a, bool causal, int pfmt, int mode, hipStream_t st) {
+  if (mode == IN_VFP8) {
+    if constexpr (__is_same(DT, BF16)) return fwd_pick_causal<DT, D, IN_VFP8>(s, a, causal, pfmt, st);
     return hipErrorInvalidValue;
   }
-  return causal ? fwd_pick_pq<DT, D, true, false>(s, a, pfmt, st)
-                : fwd_pick_pq<DT, D, false, false>(s, a, pfmt, st);
+  if (mode == IN_QKS) return fwd_pick_causal<DT, D, IN_QKS>(s, a, causal, pfmt, st);
+  return fwd_pick_causal<DT, D, IN_PLAIN>(s, a, causal, pfmt, st);
 }
 
-hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v,
-                      const float* v_scale, float sm_scale, bool causal, int pfmt, bool v_fp8,
+hipError_t launch_fwd(const Shape& s, const Inputs& in, float sm_scale, bool causal, int pfmt,
                       void* o, void* o_hp, float* lse, hipStream_t st) {
   FwdArgs a;
-  a.q = q; a.k = k; a.v = v; a.v_scale = v_scale;
+  a.q = in.q; a.k = in.k; a.v = in.v;
+  a.v_scale = in.v_scale; a.q_scale = in.q_scale; a.k_scale = in.k_scale;
   a.o = o; a.o_hp = o_hp; a.lse = lse;
   a.Nq = s.Nq; a.Nkv = s.Nkv;
   a.c = sm_scale * LOG2E;
   if (s.dtype == 0) {
-    return s.D == 128 ? fwd_pick<BF16, 128>(s, a, causal, pfmt, v_fp8, st)
-                      : fwd_pick<BF16, 64>(s, a, causal, pfmt, v_fp8, st);
+    return s.D == 128 ? fwd_pick<BF16, 128>(s, a, causal, pfmt, in.mode, st)
+                      : fwd_pick<BF16, 64>(s, a, causal, pfmt, in.mode, st);
   }
-  return s.D == 128 ? fwd_pick<FP16, 128>(s, a, causal, pfmt, v_fp8, st)
-                    : fwd_pick<FP16, 64>(s, a, causal, pfmt, v_fp8, st);
+  return s.D == 128 ? fwd_pick<FP16, 128>(s, a, causal, pfmt, in.mode, st)
+                    : fwd_pick<FP16, 64>(s, a, causal, pfmt, in.mode, st);
 }
 
 }  // namespace qat

@@ -11,13 +11,31 @@ struct Shape {
   int dtype;   // 0 bf16, 1 fp16
 };
 
+// Input modes of the attention kernels.
+//  IN_PLAIN: q, k, v hold the values (dtype).
+//  IN_VFP8:  v holds e5m2 codes, V^ = code * v_scale[b, h, d].
+//  IN_QKS:   q, k hold fp8 code values (dtype) with one fp32 scale per token
+//            (q_scale [B,H,Nq], k_scale [B,H,Nkv]); v holds values.
+enum InMode { IN_PLAIN = 0, IN_VFP8 = 1, IN_QKS = 2 };
+
+struct Inputs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* v_scale;   // IN_VFP8
+  const float* q_scale;   // IN_QKS
+  const float* k_scale;   // IN_QKS
+  int mode;
+};
+
 // pfmt: -1 = P not quantized, 0 = e4m3fn, 1 = e5m2
-hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v,
-                      const float* v_scale, float sm_scale, bool causal, int pfmt, bool v_fp8,
+hipError_t launch_fwd(const Shape& s, const Inputs& in, float sm_scale, bool causal, int pfmt,
                       void* o, void* o_hp, float* lse, hipStream_t st);
 
-// Per-token e4m3 fake quant: x [rows, D] -> xhat [rows, D] (same dtype).
-hipError_t launch_token_quant(int dtype, int D, long rows, const void* x, void* xhat, hipStream_t st);
+// Per-token e4m3 fake quant: x [rows, D] -> xhat [rows, D] (same dtype); with
+// scale_out the code values and the per-row scales are stored separately.
+hipError_t launch_token_quant(int dtype, int D, long rows, const void* x, void* xhat, float* scale_out,
+                              hipStream_t st);
 
 // Per-channel e5m2 quant of V [BH, N, D] -> codes [BH, N, D], v_scale [BH, D].
 hipError_t launch_v_quant(int dtype, int D, int BH, int N, const void* v, uint8_t* codes,
@@ -30,13 +48,11 @@ hipError_t launch_fq_rows(const float* x, int rows, int cols, int group, int fmt
 // Backward pieces.
 hipError_t launch_bwd_delta(const Shape& s, const void* o_hp, const void* dout, float* delta,
                             hipStream_t st);
-hipError_t launch_bwd_dq(const Shape& s, const void* q, const void* k, const void* v,
-                         const float* v_scale, const void* dout, const float* lse,
-                         const float* delta, float sm_scale, bool causal, int pfmt, bool v_fp8,
+hipError_t launch_bwd_dq(const Shape& s, const Inputs& in, const void* dout, const float* lse,
+                         const float* delta, float sm_scale, bool causal, int pfmt,
                          void* dq, float* p_amax, hipStream_t st);
-hipError_t launch_bwd_dkdv(const Shape& s, const void* q, const void* k, const void* v,
-                           const float* v_scale, const void* dout, const float* lse,
+hipError_t launch_bwd_dkdv(const Shape& s, const Inputs& in, const void* dout, const float* lse,
                            const float* delta, const float* p_amax, float sm_scale, bool causal,
-                           int pfmt, bool v_fp8, void* dk, void* dv, hipStream_t st);
+                           int pfmt, void* dk, void* dv, hipStream_t st);
 
 }  // namespace qat

@@ -13,10 +13,14 @@
 namespace qat {
 
 // 16 lanes per token row of D <= 128 elements: lane handles D/16 consecutive
-// elements (8 for D = 128, 4 for D = 64).
+// elements (8 for D = 128, 4 for D = 64).  With `scale_out` the row is stored
+// split: the fp8 code values (exact in bf16 and fp16) and the fp32 scale s,
+// so that x^ = code * s stays exact for the attention kernels; otherwise
+// x^ = fp32(code * s) is rounded to the storage dtype.
 template <class DT, int D>
 __global__ __launch_bounds__(256) void token_quant_kernel(const uint16_t* __restrict__ x,
-                                                          uint16_t* __restrict__ xhat, long rows) {
+                                                          uint16_t* __restrict__ xhat,
+                                                          float* __restrict__ scale_out, long rows) {
   constexpr int EPL = D / 16;   // elements per lane
   const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
@@ -38,30 +42,34 @@ __global__ __launch_bounds__(256) void token_quant_kernel(const uint16_t* __rest
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
   const FqScale fs = fq_scale(amax, Fp8Fmt<0>::FMAX);
+  const bool split = scale_out != nullptr;
+  const FqScale unit = {1.0f, fs.r};   // code value times 1: the code itself
   uint32_t outw[EPL / 2];
 #pragma unroll
   for (int e = 0; e < EPL; e += 2) {
-    f32x2 xq = fq_pair<0>(v[e], v[e + 1], fs);
+    f32x2 xq = fq_pair<0>(v[e], v[e + 1], split ? unit : fs);
     if (fs.r == 0.0f) xq = (f32x2){0.0f, 0.0f};   // zero group: +0, not -0
     outw[e / 2] = DT::pack2(xq[0], xq[1]);
   }
   if (!valid) return;
+  if (split && sub == 0) scale_out[row] = fs.s;
   uint16_t* dst = xhat + row * D + sub * EPL;
   if constexpr (EPL == 8) *reinterpret_cast<u32x4*>(dst) = (u32x4){outw[0], outw[1], outw[2], outw[3]};
   else *reinterpret_cast<u32x2*>(dst) = (u32x2){outw[0], outw[1]};
 }
 
-hipError_t launch_token_quant(int dtype, int D, long rows, const void* x, void* xhat, hipStream_t st) {
+hipError_t launch_token_quant(int dtype, int D, long rows, const void* x, void* xhat, float* scale_out,
+                              hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   dim3 grid((unsigned)((rows + 15) / 16));
   const uint16_t* xi = (const uint16_t*)x;
   uint16_t* xo = (uint16_t*)xhat;
   if (dtype == 0) {
-    if (D == 128) hipLaunchKernelGGL((token_quant_kernel<BF16, 128>), grid, dim3(256), 0, st, xi, xo, rows);
-    else hipLaunchKernelGGL((token_quant_kernel<BF16, 64>), grid, dim3(256), 0, st, xi, xo, rows);
+    if (D == 128) hipLaunchKernelGGL((token_quant_kernel<BF16, 128>), grid, dim3(256), 0, st, xi, xo, scale_out, rows);
+    else hipLaunchKernelGGL((token_quant_kernel<BF16, 64>), grid, dim3(256), 0, st, xi, xo, scale_out, rows);
   } else {
-    if (D == 128) hipLaunchKernelGGL((token_quant_kernel<FP16, 128>), grid, dim3(256), 0, st, xi, xo, rows);
-    else hipLaunchKernelGGL((token_quant_kernel<FP16, 64>), grid, dim3(256), 0, st, xi, xo, rows);
+    if (D == 128) hipLaunchKernelGGL((token_quant_kernel<FP16, 128>), grid, dim3(256), 0, st, xi, xo, scale_out, rows);
+    else hipLaunchKernelGGL((token_quant_kernel<FP16, 64>), grid, dim3(256), 0, st, xi, xo, scale_out, rows);
   }
   return hipGetLastError();
 }

@@ -23,6 +23,8 @@ QAT_P_QUANT = 1 << 0
 QAT_P_E5M2 = 1 << 1
 QAT_QKV_QUANT = 1 << 2
 QAT_V_FP8_E5M2 = 1 << 3
+QAT_BWD_PREPARE, QAT_BWD_DELTA, QAT_BWD_DQ, QAT_BWD_DKDV = 1, 2, 4, 8
+QAT_BWD_ALL = 15
 
 _DTYPES = {torch.bfloat16: QAT_DTYPE_BF16, torch.float16: QAT_DTYPE_FP16}
 
@@ -62,6 +64,9 @@ def lib():
     L.qat_attn_fwd.restype = ctypes.c_int
     L.qat_attn_bwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, f32, ctypes.c_int, u32, vp, vp, vp, vp, sz, vp]
     L.qat_attn_bwd.restype = ctypes.c_int
+    L.qat_attn_bwd_stages.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, f32, ctypes.c_int, u32, vp, vp, vp, vp, sz,
+                                      u32, vp]
+    L.qat_attn_bwd_stages.restype = ctypes.c_int
     L.qat_attn_workspace_bytes.argtypes = [dp, u32, ctypes.c_int]
     L.qat_attn_workspace_bytes.restype = sz
     L.qat_quant_v_fp8.argtypes = [dp, vp, vp, vp, vp]
@@ -137,8 +142,9 @@ def attn_fwd(q, k, v, sm_scale, causal=False, quant_flags=QAT_P_QUANT, v_scale=N
 
 
 def attn_bwd(q, k, v, o_hp, lse, dout, sm_scale, causal=False, quant_flags=QAT_P_QUANT,
-             v_scale=None, out=None, workspace=None):
-    """Straight-through backward: returns (dq, dk, dv)."""
+             v_scale=None, out=None, workspace=None, stages=QAT_BWD_ALL):
+    """Straight-through backward: returns (dq, dk, dv).  ``stages`` selects a
+    subset of the backward stages (qat_attn_bwd_stages)."""
     _need(q, "q")
     _need(k, "k", q.dtype)
     _need(v, "v", torch.uint8 if quant_flags & QAT_V_FP8_E5M2 else q.dtype)
@@ -155,10 +161,11 @@ def attn_bwd(q, k, v, o_hp, lse, dout, sm_scale, causal=False, quant_flags=QAT_P
     nbytes = workspace_bytes(dims, quant_flags, 1)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 256), device=q.device, dtype=torch.uint8)
-    st = lib().qat_attn_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(v_scale), _ptr(o_hp),
-                            _ptr(lse), _ptr(dout), float(sm_scale), int(bool(causal)), quant_flags,
-                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream())
-    _check("qat_attn_bwd", st)
+    st = lib().qat_attn_bwd_stages(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(v_scale), _ptr(o_hp),
+                                   _ptr(lse), _ptr(dout), float(sm_scale), int(bool(causal)), quant_flags,
+                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), stages,
+                                   _stream())
+    _check("qat_attn_bwd_stages", st)
     return dq, dk, dv
 
 

@@ -79,6 +79,11 @@ def test_bwd_validation(L):
     need = ops.workspace_bytes(D(1, 1, 16, 16, 64, 0), ops.QAT_P_QUANT, 1)
     assert bwd(D(1, 1, 16, 16, 64, 0), FAKE, need - 1) == ops.QAT_EWORKSPACE
     assert bwd(D(1, 1, 16, 16, 80, 0), FAKE, need) == ops.QAT_EUNSUPPORTED
+    # staged backward: an empty or unknown stage mask is rejected
+    for mask in (0, 1 << 6):
+        assert L.qat_attn_bwd_stages(ctypes.byref(D(1, 1, 16, 16, 64, 0)), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                                     0.125, 0, ops.QAT_P_QUANT, FAKE, FAKE, FAKE, FAKE, need, mask,
+                                     None) == ops.QAT_EINVAL
 
 
 def test_workspace_layout():
@@ -90,7 +95,7 @@ def test_workspace_layout():
     amax = up(2 * 3 * 3 * 100 * 4)            # ceil(130 / 64) = 3 groups
     assert ops.workspace_bytes(d, 0, 1) == delta
     assert ops.workspace_bytes(d, ops.QAT_P_QUANT, 1) == delta + amax
-    qkv = up(6 * 100 * 128 * 2) + 2 * up(6 * 130 * 128 * 2)
+    qkv = up(6 * 100 * 128 * 2) + 2 * up(6 * 130 * 128 * 2) + up(6 * 100 * 4) + up(6 * 130 * 4)
     assert ops.workspace_bytes(d, ops.QAT_P_QUANT | ops.QAT_QKV_QUANT, 0) == qkv
     assert ops.workspace_bytes(d, ops.QAT_P_QUANT | ops.QAT_QKV_QUANT, 1) == delta + amax + qkv
     assert ops.workspace_bytes(d, 0, 2) == 0

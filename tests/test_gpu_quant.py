@@ -83,24 +83,37 @@ def test_fake_quant_rows_exhaustive_ratio_sweep():
 
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp16", 64), ("bf16", 64)])
 def test_token_quant_matches_oracle(dtype, D):
-    # the per-token pre-pass stores x^ in the input dtype: compare with the
-    # oracle's fp32 x^ rounded to that dtype (RNE), bit for bit
+    # The per-token pre-pass keeps Q and K split into fp8 code values (exact
+    # in the dtype) and fp32 scales, and V as x^ rounded to the dtype (RNE).
+    # Workspace layout of the forward: q codes, k codes, v^, q scales, k scales.
     from quantization_aware_attention_amd import ops
     from tests._harness import to_dev
-    w = W.WORKLOADS["long_video"].with_(B=1, H=3, Nq=77, Nkv=77, D=D, dtype=dtype)
+    w = W.WORKLOADS["long_video"].with_(B=1, H=3, Nq=77, Nkv=45, D=D, dtype=dtype)
     inp = W.make_inputs(w)
     q = to_dev(inp["q_bits"], dtype)
     k = to_dev(inp["k_bits"], dtype)
     v = to_dev(inp["v_bits"], dtype)
+    flags = ops.QAT_QKV_QUANT | ops.QAT_P_QUANT
     dims = ops.dims_of(q, k)
-    ws = torch.zeros(ops.workspace_bytes(dims, ops.QAT_QKV_QUANT | ops.QAT_P_QUANT, 0), dtype=torch.uint8, device="cuda")
-    ops.attn_fwd(q, k, v, w.sm_scale, False, ops.QAT_QKV_QUANT | ops.QAT_P_QUANT, workspace=ws)
+    ws = torch.zeros(ops.workspace_bytes(dims, flags, 0), dtype=torch.uint8, device="cuda")
+    ops.attn_fwd(q, k, v, w.sm_scale, False, flags, workspace=ws)
     torch.cuda.synchronize()
-    n = q.numel() * 2
-    qh_gpu = ws[:n].cpu().numpy().view(np.uint16).reshape(q.shape)
-    _, _, xhat = oracle.quantize_token_rows(inp["q"], "e4m3")
+    wsn = ws.cpu().numpy()
+    up = lambda x: -(-x // 256) * 256
+    off = 0
+    pieces = {}
+    for name, nbytes in (("q", q.numel() * 2), ("k", k.numel() * 2), ("v", v.numel() * 2),
+                         ("qs", q.numel() // D * 4), ("ks", k.numel() // D * 4)):
+        pieces[name] = wsn[off:off + nbytes]
+        off += up(nbytes)
+    for name in ("q", "k"):
+        codes, scales, _ = oracle.quantize_token_rows(inp[name], "e4m3")
+        _, code_bits = W.round_to_dtype(fp8.decode(codes, "e4m3"), dtype)
+        assert np.array_equal(pieces[name].view(np.uint16).reshape(code_bits.shape), code_bits)
+        assert np.array_equal(pieces[name + "s"].view(np.float32).reshape(scales.shape), scales)
+    _, _, xhat = oracle.quantize_token_rows(inp["v"], "e4m3")
     _, ref_bits = W.round_to_dtype(xhat.astype(np.float64), dtype)
-    assert np.array_equal(qh_gpu, ref_bits)
+    assert np.array_equal(pieces["v"].view(np.uint16).reshape(ref_bits.shape), ref_bits)
 
 
 @pytest.mark.parametrize("N", [512, 500, 1])
