@@ -132,14 +132,16 @@ constexpr int DQ_BM = 128;
 constexpr int DQ_BN = 64;
 
 template <class DT, int D, bool CAUSAL, int PQ, int IN>
-__global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   constexpr bool VFP8 = IN == IN_VFP8;
   constexpr bool QKS = IN == IN_QKS;
   constexpr int TILE = DQ_BN * D * 2;
   constexpr int NDB = D / 32;
   constexpr int NKS = D / 16;
-  __shared__ __attribute__((aligned(16))) char smem[2][TILE];   // K, V of the current tile
-  __shared__ __attribute__((aligned(16))) float ks_s[DQ_BN];     // IN_QKS: key scales
+  constexpr int CH = D / 8;
+  constexpr int LPT = DQ_BN * CH / 256;
+  __shared__ __attribute__((aligned(16))) char smem[2][2][TILE];   // [buffer][K, V]
+  __shared__ __attribute__((aligned(16))) float ks_s[2][DQ_BN];     // IN_QKS: key scales
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int bh = blockIdx.y;
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
   const int Nq = a.Nq, Nkv = a.Nkv;
   const uint16_t* qp = (const uint16_t*)a.q + (size_t)bh * Nq * D;
   const uint16_t* dop = (const uint16_t*)a.dout + (size_t)bh * Nq * D;
-  const uint8_t* kp = (const uint8_t*)a.k + (size_t)bh * Nkv * D * 2;
+  const uint16_t* kp = (const uint16_t*)a.k + (size_t)bh * Nkv * D;
   const uint8_t* vp = (const uint8_t*)a.v + (size_t)bh * Nkv * D * (VFP8 ? 1 : 2);
   const float* vsc = VFP8 ? a.v_scale + (size_t)bh * D : nullptr;
 
@@ -169,20 +171,64 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dq_acc[db] = (f32x16){};
 
+  // K tiles (and V, unless fp8) go HBM -> LDS directly, double-buffered; fp8
+  // V codes and key scales take a register detour.
+  u32x2 vcode[LPT];
+  float ksreg = 0.0f;
+  auto issue_tile = [&](int t, int buf) {
+    tile_to_lds_async<D, DQ_BN, 4>(smem[buf][0], kp, t * DQ_BN, Nkv, w, lane);
+    if constexpr (VFP8) {
+#pragma unroll
+      for (int u = 0; u < LPT; ++u) {
+        const int idx = tid + 256 * u, row = idx / CH, ch = idx % CH;
+        const int key = min(t * DQ_BN + row, Nkv - 1);
+        vcode[u] = *reinterpret_cast<const u32x2*>(vp + (size_t)key * D + ch * 8);
+      }
+    } else {
+      tile_to_lds_async<D, DQ_BN, 4>(smem[buf][1], (const uint16_t*)vp, t * DQ_BN, Nkv, w, lane);
+    }
+    if constexpr (QKS) {
+      const int key = t * DQ_BN + tid;
+      if (tid < DQ_BN) ksreg = key < Nkv ? a.k_scale[(size_t)bh * Nkv + key] : 0.0f;
+    }
+  };
+  auto finish_tile = [&](int buf) {
+    if constexpr (VFP8) {   // V^ = code * v_scale[d], rounded to bf16
+#pragma unroll
+      for (int u = 0; u < LPT; ++u) {
+        const int idx = tid + 256 * u, row = idx / CH, ch = idx % CH;
+        const f32x4 s0 = *reinterpret_cast<const f32x4*>(vsc + ch * 8);
+        const f32x4 s1 = *reinterpret_cast<const f32x4*>(vsc + ch * 8 + 4);
+        const float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+        u32x4 vv;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const f32x2 f = __builtin_amdgcn_cvt_pk_f32_bf8((int)(vcode[u][h >> 1] >> (16 * (h & 1))), false);
+          vv[h] = BF16::pack2(f[0] * sc[2 * h], f[1] * sc[2 * h + 1]);
+        }
+        *reinterpret_cast<u32x4*>(smem[buf][1] + tile_off<D>(row, ch)) = vv;
+      }
+    }
+    if constexpr (QKS) {
+      if (tid < DQ_BN) ks_s[buf][tid] = ksreg;
+    }
+  };
+
   const int kv_end = CAUSAL ? min(Nkv, qb + DQ_BM) : Nkv;
   const int ntiles = (kv_end + DQ_BN - 1) / DQ_BN;
+  if (ntiles > 0) {
+    issue_tile(0, 0);
+    wait_vmem();
+    finish_tile(0);
+  }
+  __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int kv0 = t * DQ_BN;
-    __syncthreads();
-    stage_kv_tile<DT, D, false>(smem[0], kp, nullptr, kv0, Nkv, tid);
-    stage_kv_tile<DT, D, VFP8>(smem[1], vp, vsc, kv0, Nkv, tid);
-    if constexpr (QKS) {
-      if (tid < DQ_BN) ks_s[tid] = kv0 + tid < Nkv ? a.k_scale[(size_t)bh * Nkv + kv0 + tid] : 0.0f;
-    }
-    __syncthreads();
-    if (q0 >= Nq || (CAUSAL && kv0 > q0 + 31)) continue;
-    const char* Kt = smem[0];
-    const char* Vt = smem[1];
+    const int buf = t & 1;
+    if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
+    if (q0 < Nq && !(CAUSAL && kv0 > q0 + 31)) {
+    const char* Kt = smem[buf][0];
+    const char* Vt = smem[buf][1];
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -195,18 +241,14 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
       }
     }
     const bool need_mask = (kv0 + DQ_BN > Nkv) || (CAUSAL && kv0 + DQ_BN - 1 > q0);
-    float sk[2][16];
     if constexpr (QKS) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const f32x4 v4 = *reinterpret_cast<const f32x4*>(&ks_s[kb * 32 + 8 * u + 4 * g]);
+          const f32x4 v4 = *reinterpret_cast<const f32x4*>(&ks_s[buf][kb * 32 + 8 * u + 4 * g]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sk[kb][4 * u + e] = v4[e];
-            s[kb][4 * u + e] *= v4[e];
-          }
+          for (int e = 0; e < 4; ++e) s[kb][4 * u + e] *= v4[e];
         }
     }
     float p[2][16];
@@ -237,8 +279,9 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
         const int r0 = 8 * h + 2 * jj;
         float d0 = p[kb][r0] * (dp[kb][r0] - Di), d1 = p[kb][r0 + 1] * (dp[kb][r0 + 1] - Di);
         if constexpr (QKS) {   // dQ = sm_scale sum_j dS_ij s_k[j] code_k[j]
-          d0 *= sk[kb][r0];
-          d1 *= sk[kb][r0 + 1];
+          const f32x2 k2 = *reinterpret_cast<const f32x2*>(&ks_s[buf][kb * 32 + 8 * (r0 >> 2) + 4 * g + (r0 & 3)]);
+          d0 *= k2[0];
+          d1 *= k2[1];
         }
         w4[jj] = DT::pack2(d0, d1);
       }
@@ -247,6 +290,10 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
       for (int db = 0; db < NDB; ++db)
         dq_acc[db] = DT::mfma(lds_tr8<D>(Kt, kk * 16, db * 32, lane), ds_op, dq_acc[db]);
     }
+    }
+    wait_vmem();
+    if (t + 1 < ntiles) finish_tile(buf ^ 1);
+    __syncthreads();
   }
   // causal rows whose every later tile was skipped still record zero-free
   // groups only for tiles they visited; the dK/dV kernel never reads the
@@ -277,13 +324,13 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   constexpr int NKS = D / 16;
   constexpr int CH = D / 8;
   constexpr int LPT = DKV_BQ * CH / 256;
-  __shared__ __attribute__((aligned(16))) char qt_s[TILE];
-  __shared__ __attribute__((aligned(16))) char dot_s[TILE];
-  __shared__ __attribute__((aligned(16))) float m_s[DKV_BQ];
-  __shared__ __attribute__((aligned(16))) float d_s[DKV_BQ];
-  __shared__ __attribute__((aligned(16))) float sq_s[DKV_BQ];      // IN_QKS: query scales
-  __shared__ __attribute__((aligned(16))) float qs_s[2][DKV_BQ];   // P-quant s per (group, query)
-  __shared__ __attribute__((aligned(16))) float qr_s[2][DKV_BQ];   // P-quant r
+  __shared__ __attribute__((aligned(16))) char qt_s[2][TILE];
+  __shared__ __attribute__((aligned(16))) char dot_s[2][TILE];
+  __shared__ __attribute__((aligned(16))) float m_s[2][DKV_BQ];
+  __shared__ __attribute__((aligned(16))) float d_s[2][DKV_BQ];
+  __shared__ __attribute__((aligned(16))) float sq_s[2][DKV_BQ];      // IN_QKS: query scales
+  __shared__ __attribute__((aligned(16))) float qs_s[2][2][DKV_BQ];   // P-quant s per (group, query)
+  __shared__ __attribute__((aligned(16))) float qr_s[2][2][DKV_BQ];   // P-quant r
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int bh = blockIdx.y;
@@ -325,7 +372,6 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
       }
     }
   }
-
   const float sk_lane = QKS ? (kj < Nkv ? a.k_scale[(size_t)bh * Nkv + kj] : 0.0f) : 1.0f;
 
   f32x16 dk_acc[NDB], dv_acc[NDB];
@@ -335,44 +381,58 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     dv_acc[db] = (f32x16){};
   }
 
-  const int qt_begin = CAUSAL ? (k0 / DKV_BQ) : 0;
-  const int ntq = (Nq + DKV_BQ - 1) / DKV_BQ;
-  const bool wave_live = k0w < Nkv;
-  for (int t = qt_begin; t < ntq; ++t) {
+  // Q and dO tiles go HBM -> LDS directly (double-buffered); the per-query
+  // vectors (log2-domain LSE, Delta, Q scales, P-quant scales of this
+  // workgroup's two key groups) are staged through registers.
+  float vec0 = 0.0f, vec1 = 0.0f, vec2 = 0.0f;
+  auto issue_tile = [&](int t, int buf) {
     const int qt0 = t * DKV_BQ;
-    __syncthreads();
-    // ---- stage Q, dO tiles and per-query vectors
-#pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int idx = tid + 256 * u, row = idx / CH, ch = idx % CH;
-      const int q = qt0 + row;
-      u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
-      if (q < Nq) {
-        x = *reinterpret_cast<const u32x4*>(qp + (size_t)q * D + ch * 8);
-        y = *reinterpret_cast<const u32x4*>(dop + (size_t)q * D + ch * 8);
-      }
-      *reinterpret_cast<u32x4*>(qt_s + tile_off<D>(row, ch)) = x;
-      *reinterpret_cast<u32x4*>(dot_s + tile_off<D>(row, ch)) = y;
-    }
+    tile_to_lds_async<D, DKV_BQ, 4>(qt_s[buf], qp, qt0, Nq, w, lane);
+    tile_to_lds_async<D, DKV_BQ, 4>(dot_s[buf], dop, qt0, Nq, w, lane);
     if (tid < DKV_BQ) {
       const int q = qt0 + tid;
-      m_s[tid] = q < Nq ? a.lse[(size_t)bh * Nq + q] * LOG2E : 0.0f;
-      d_s[tid] = q < Nq ? a.delta[(size_t)bh * Nq + q] : 0.0f;
-      if constexpr (QKS) sq_s[tid] = q < Nq ? a.q_scale[(size_t)bh * Nq + q] : 1.0f;
+      vec0 = q < Nq ? a.lse[(size_t)bh * Nq + q] * LOG2E : 0.0f;
+      vec1 = q < Nq ? a.delta[(size_t)bh * Nq + q] : 0.0f;
+      if constexpr (QKS) vec2 = q < Nq ? a.q_scale[(size_t)bh * Nq + q] : 1.0f;
     } else if constexpr (PQ >= 0) {
       if (tid < 3 * DKV_BQ) {
         const int e = tid - DKV_BQ, gi = e / DKV_BQ, qq = e % DKV_BQ;
         const int q = qt0 + qq, grp = grp0 + gi;
-        float amax = 0.0f;
-        if (q < Nq && grp < a.NG) amax = a.p_amax_in[((size_t)bh * a.NG + grp) * Nq + q];
-        const FqScale fs = fq_scale(amax, Fp8Fmt<(PQ >= 0 ? PQ : 0)>::FMAX);
-        qs_s[gi][qq] = fs.s;
-        qr_s[gi][qq] = fs.r;
+        vec0 = (q < Nq && grp < a.NG) ? a.p_amax_in[((size_t)bh * a.NG + grp) * Nq + q] : 0.0f;
       }
     }
-    __syncthreads();
-    if (!wave_live) continue;
+  };
+  auto finish_tile = [&](int buf) {
+    if (tid < DKV_BQ) {
+      m_s[buf][tid] = vec0;
+      d_s[buf][tid] = vec1;
+      if constexpr (QKS) sq_s[buf][tid] = vec2;
+    } else if constexpr (PQ >= 0) {
+      if (tid < 3 * DKV_BQ) {
+        const int e = tid - DKV_BQ, gi = e / DKV_BQ, qq = e % DKV_BQ;
+        const FqScale fs = fq_scale(vec0, Fp8Fmt<(PQ >= 0 ? PQ : 0)>::FMAX);
+        qs_s[buf][gi][qq] = fs.s;
+        qr_s[buf][gi][qq] = fs.r;
+      }
+    }
+  };
 
+  const int qt_begin = CAUSAL ? (k0 / DKV_BQ) : 0;
+  const int ntq = (Nq + DKV_BQ - 1) / DKV_BQ;
+  const bool wave_live = k0w < Nkv;
+  if (qt_begin < ntq) {
+    issue_tile(qt_begin, qt_begin & 1);
+    wait_vmem();
+    finish_tile(qt_begin & 1);
+  }
+  __syncthreads();
+  for (int t = qt_begin; t < ntq; ++t) {
+    const int qt0 = t * DKV_BQ;
+    const int buf = t & 1;
+    if (t + 1 < ntq) issue_tile(t + 1, buf ^ 1);
+    if (wave_live) {
+    const char* Qt = qt_s[buf];
+    const char* dOt = dot_s[buf];
 #pragma unroll
     for (int qb2 = 0; qb2 < DKV_BQ / 32; ++qb2) {
       const int qs = qt0 + qb2 * 32;          // first query of this 32-block
@@ -382,23 +442,23 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
       f32x16 s = (f32x16){}, dp = (f32x16){};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        s = DT::mfma(lds_row8<D>(qt_s, qb2 * 32 + l32, 2 * ks + g), kf[ks], s);
-        dp = DT::mfma(lds_row8<D>(dot_s, qb2 * 32 + l32, 2 * ks + g), vf[ks], dp);
+        s = DT::mfma(lds_row8<D>(Qt, qb2 * 32 + l32, 2 * ks + g), kf[ks], s);
+        dp = DT::mfma(lds_row8<D>(dOt, qb2 * 32 + l32, 2 * ks + g), vf[ks], dp);
       }
       const bool need_mask = (qs + 32 > Nq) || (k0w + 32 > Nkv) || (CAUSAL && qs < k0w + 31);
       float p[16], pq[16], dsv[16];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int ql = qb2 * 32 + 8 * u + 4 * g;   // local query index of registers 4u..4u+3
-        const f32x4 mv = *reinterpret_cast<const f32x4*>(&m_s[ql]);
-        const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&d_s[ql]);
+        const f32x4 mv = *reinterpret_cast<const f32x4*>(&m_s[buf][ql]);
+        const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&d_s[buf][ql]);
         f32x4 sv = {0, 0, 0, 0}, rv = {0, 0, 0, 0};
         if constexpr (PQ >= 0) {
-          sv = *reinterpret_cast<const f32x4*>(&qs_s[mygrp][ql]);
-          rv = *reinterpret_cast<const f32x4*>(&qr_s[mygrp][ql]);
+          sv = *reinterpret_cast<const f32x4*>(&qs_s[buf][mygrp][ql]);
+          rv = *reinterpret_cast<const f32x4*>(&qr_s[buf][mygrp][ql]);
         }
         f32x4 sq4 = {1.0f, 1.0f, 1.0f, 1.0f};
-        if constexpr (QKS) sq4 = *reinterpret_cast<const f32x4*>(&sq_s[ql]);
+        if constexpr (QKS) sq4 = *reinterpret_cast<const f32x4*>(&sq_s[buf][ql]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * u + e;
@@ -440,11 +500,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
         const s16x8 ds_op = __builtin_bit_cast(s16x8, (u32x4){wd[0], wd[1], wd[2], wd[3]});
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          dv_acc[db] = DT::mfma(lds_tr8<D>(dot_s, qb2 * 32 + 16 * h, db * 32, lane), p_op, dv_acc[db]);
-          dk_acc[db] = DT::mfma(lds_tr8<D>(qt_s, qb2 * 32 + 16 * h, db * 32, lane), ds_op, dk_acc[db]);
+          dv_acc[db] = DT::mfma(lds_tr8<D>(dOt, qb2 * 32 + 16 * h, db * 32, lane), p_op, dv_acc[db]);
+          dk_acc[db] = DT::mfma(lds_tr8<D>(Qt, qb2 * 32 + 16 * h, db * 32, lane), ds_op, dk_acc[db]);
         }
       }
     }
+    }
+    wait_vmem();
+    if (t + 1 < ntq) finish_tile(buf ^ 1);
+    __syncthreads();
   }
 
   if (kj >= Nkv) return;

@@ -46,7 +46,7 @@ constexpr int FWD_BN = 64;       // keys per tile (= P_GROUP)
 constexpr float RESCALE_SLACK = 8.0f;
 
 template <class DT, int D, bool CAUSAL, int PQ, int IN>
-__global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   constexpr bool VFP8 = IN == IN_VFP8;
   constexpr bool QKS = IN == IN_QKS;
   constexpr int CH = D / 8;                 // 16-byte chunks per row
@@ -83,39 +83,34 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
   const int kv_end = CAUSAL ? min(Nkv, qb + FWD_BM) : Nkv;
   const int ntiles = (kv_end + FWD_BN - 1) / FWD_BN;
 
-  u32x4 kreg[LPT];
-  u32x4 vreg[LPT];
+  // V codes of the fp8-V path take a register detour (decoded to bf16 on the
+  // way into LDS); every other tile goes HBM -> LDS directly.
   u32x2 vcode[LPT];
   float ksreg = 0.0f;
-  auto load_regs = [&](int t) {
+  auto issue_tile = [&](int t, int buf) {
+    tile_to_lds_async<D, FWD_BN, 4>(smem[buf][0], kp, t * FWD_BN, Nkv, w, lane);
+    if constexpr (VFP8) {
+#pragma unroll
+      for (int u = 0; u < LPT; ++u) {
+        const int idx = tid + 256 * u, row = idx / CH, ch = idx % CH;
+        const int key = min(t * FWD_BN + row, Nkv - 1);
+        vcode[u] = *reinterpret_cast<const u32x2*>(vp8 + (size_t)key * D + ch * 8);
+      }
+    } else {
+      tile_to_lds_async<D, FWD_BN, 4>(smem[buf][1], (const uint16_t*)vp8, t * FWD_BN, Nkv, w, lane);
+    }
     if constexpr (QKS) {
       const int key = t * FWD_BN + tid;
       if (tid < FWD_BN) ksreg = key < Nkv ? ksp[key] : 0.0f;
     }
-#pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int idx = tid + 256 * u, row = idx / CH, ch = idx % CH;
-      const int key = t * FWD_BN + row;
-      const bool ok = key < Nkv;
-      kreg[u] = ok ? *reinterpret_cast<const u32x4*>(kp + (size_t)key * D + ch * 8) : (u32x4){0, 0, 0, 0};
-      if constexpr (VFP8) {
-        vcode[u] = ok ? *reinterpret_cast<const u32x2*>(vp8 + (size_t)key * D + ch * 8) : (u32x2){0, 0};
-      } else {
-        vreg[u] = ok ? *reinterpret_cast<const u32x4*>(vp8 + ((size_t)key * D + ch * 8) * 2) : (u32x4){0, 0, 0, 0};
-      }
-    }
   };
-  auto store_regs = [&](int buf) {
-    if constexpr (QKS) {
-      if (tid < FWD_BN) ks_s[buf][tid] = ksreg;
-    }
+  // register-staged parts of a tile: written after the loads landed
+  auto finish_tile = [&](int buf) {
+    if constexpr (VFP8) {
 #pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int idx = tid + 256 * u, row = idx / CH, ch = idx % CH;
-      *reinterpret_cast<u32x4*>(smem[buf][0] + tile_off<D>(row, ch)) = kreg[u];
-      if constexpr (VFP8) {
-        // e5m2 codes -> bf16 (exact: every e5m2 value is a bf16 value)
-        u32x4 vv;
+      for (int u = 0; u < LPT; ++u) {
+        const int idx = tid + 256 * u, row = idx / CH, ch = idx % CH;
+        u32x4 vv;   // e5m2 codes -> bf16 (exact: every e5m2 value is a bf16 value)
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
           const uint32_t word = vcode[u][h >> 1] >> (16 * (h & 1));
@@ -123,9 +118,10 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
           vv[h] = BF16::pack2(f[0], f[1]);
         }
         *reinterpret_cast<u32x4*>(smem[buf][1] + tile_off<D>(row, ch)) = vv;
-      } else {
-        *reinterpret_cast<u32x4*>(smem[buf][1] + tile_off<D>(row, ch)) = vreg[u];
       }
+    }
+    if constexpr (QKS) {
+      if (tid < FWD_BN) ks_s[buf][tid] = ksreg;
     }
   };
 
@@ -139,14 +135,15 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
   }
 
   if (ntiles > 0) {
-    load_regs(0);
-    store_regs(0);
+    issue_tile(0, 0);
+    wait_vmem();
+    finish_tile(0);
   }
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < ntiles) load_regs(t + 1);
+    if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
     const int kv0 = t * FWD_BN;
     const bool active = (q0 < Nq) && (!CAUSAL || kv0 <= q0 + 31);
     if (active) {
@@ -247,7 +244,8 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
         }
       }
     }
-    if (t + 1 < ntiles) store_regs(buf ^ 1);
+    wait_vmem();
+    if (t + 1 < ntiles) finish_tile(buf ^ 1);
     __syncthreads();
   }
 

@@ -110,6 +110,36 @@ __device__ __forceinline__ s16x8 lds_tr8(const char* tile, int row0, int col0, i
   return (s16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Asynchronous copy of one [BN x D] 16-bit tile from HBM into the swizzled LDS
+// layout with global_load_lds_dwordx4: every wave instruction fills one
+// contiguous KiB of LDS (lane l -> bytes 16l..16l+15), so lane l fetches the
+// global chunk that belongs at that LDS position.  Rows past `nrows` are
+// clamped to the last valid row (finite data; the kernels mask those keys).
+// Each of the NW waves issues (BN*D*2/1024)/NW instructions.
+template <int D, int BN, int NW>
+__device__ __forceinline__ void tile_to_lds_async(char* lds_tile, const uint16_t* src, int row0, int nrows,
+                                                  int wave, int lane) {
+  constexpr int ROW_BYTES = D * 2;
+  constexpr int CPR = ROW_BYTES / 16;                 // chunks per row
+  constexpr int ROWS_PER_KIB = 1024 / ROW_BYTES;
+  constexpr int KIB = BN * ROW_BYTES / 1024;
+  static_assert(KIB % NW == 0, "tile must split evenly over the waves");
+#pragma unroll
+  for (int u = 0; u < KIB / NW; ++u) {
+    const int blk = wave * (KIB / NW) + u;
+    const int row = blk * ROWS_PER_KIB + lane / CPR;
+    const int chunk = (lane % CPR) ^ swz<D>(row);
+    const int grow = min(row0 + row, nrows - 1);
+    const uint16_t* g = src + (size_t)grow * D + chunk * 8;
+    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(lds_tile + blk * 1024), 16, 0, 0);
+  }
+}
+
+// Wait for this wave's outstanding global loads (including LDS DMA).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
 // ---------------------------------------------------------------- FQ
 // One group's scale pair: s = fp32(a/FMAX), r = fp32(FMAX/a), both correctly
 // rounded divisions; a == 0 or an r that overflows gives s = r = 0 (the group
