@@ -15,14 +15,15 @@
 //    dQ^T = K^T dS^T reads K^T through ds_read_b64_tr_b16.  Because a lane
 //    holds a query row's 64-key group, this kernel also records the P-quant
 //    absmax of every (row, group) for the dK/dV kernel.
-//  * dK/dV kernel: a workgroup of 4 waves owns 128 keys (two P groups); each
-//    wave keeps its 32 keys' K^T and V^T in registers and computes S = Q K^T
-//    and dP = dO V^T with one lane per key, so P^ and dS are already the
-//    operands of dV^T = dO^T P^ and dK^T = Q^T dS (Q and dO tiles go through
-//    LDS, read row-major for S/dP and transposed for dV/dK).  A key-per-lane
-//    layout has a query's 64 keys spread over 64 lanes of two waves; reading
-//    the absmax recorded by the dQ kernel replaces that cross-lane
-//    reduction.
+//  * dK/dV kernel: a workgroup of 8 waves owns 128 keys (two P groups);
+//    each wave keeps its 32 keys' K^T (and V^T) in registers and computes
+//    S = Q K^T (and dP = dO V^T) with one lane per key, so P^ and dS are
+//    already the operands of dV^T = dO^T P^ and dK^T = Q^T dS (Q and dO
+//    tiles go through LDS, read row-major for S/dP and transposed for dV/dK).
+//    Half the waves accumulate dV, half dK, so each holds one accumulator.
+//    A key-per-lane layout has a query's 64 keys spread over 64 lanes of two
+//    waves; reading the absmax recorded by the dQ kernel replaces that
+//    cross-lane reduction.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -312,18 +313,22 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ dK / dV
-constexpr int DKV_BN = 128;   // keys per workgroup (two P groups)
+// Eight waves share one block of 128 keys (two P groups) and the staged Q /
+// dO tiles: waves 0-3 ("dV waves") form S, P and the fake-quantized P^ for
+// their 32 keys and accumulate dV^T = dO^T P^; waves 4-7 ("dK waves") form S,
+// P, dP = dO V^T and dS and accumulate dK^T = Q^T dS.  S is formed by both
+// halves (identically), which costs one extra QK^T per block but leaves every
+// wave a single 64-register accumulator, so two waves fit on each SIMD.
+constexpr int DKV_BN = 128;   // keys per workgroup
 constexpr int DKV_BQ = 64;    // queries per staged tile
 
 template <class DT, int D, bool CAUSAL, int PQ, int IN>
-__global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdArgs a) {
   constexpr bool VFP8 = IN == IN_VFP8;
   constexpr bool QKS = IN == IN_QKS;
   constexpr int TILE = DKV_BQ * D * 2;
   constexpr int NDB = D / 32;
   constexpr int NKS = D / 16;
-  constexpr int CH = D / 8;
-  constexpr int LPT = DKV_BQ * CH / 256;
   __shared__ __attribute__((aligned(16))) char qt_s[2][TILE];
   __shared__ __attribute__((aligned(16))) char dot_s[2][TILE];
   __shared__ __attribute__((aligned(16))) float m_s[2][DKV_BQ];
@@ -333,28 +338,32 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float qr_s[2][2][DKV_BQ];   // P-quant r
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const bool dk_wave = w >= 4;
+  const int kw = w & 3;
   const int bh = blockIdx.y;
   const int k0 = blockIdx.x * DKV_BN;
-  const int k0w = k0 + w * 32;
+  const int k0w = k0 + kw * 32;
   const int kj = k0w + l32;
   const int Nq = a.Nq, Nkv = a.Nkv;
   const int grp0 = k0 / 64;
-  const int mygrp = w >> 1;
+  const int mygrp = kw >> 1;
   const uint16_t* qp = (const uint16_t*)a.q + (size_t)bh * Nq * D;
   const uint16_t* dop = (const uint16_t*)a.dout + (size_t)bh * Nq * D;
   const uint16_t* kp = (const uint16_t*)a.k + (size_t)bh * Nkv * D;
 
-  // K^T and V^T operands of this wave's 32 keys: lane holds key kj, d = 16ks + 8g .. +7
+  // K^T (every wave) and V^T (dK waves) operands of this wave's 32 keys:
+  // lane holds key kj, d = 16ks + 8g .. +7
   s16x8 kf[NKS], vf[NKS];
   {
     const bool ok = kj < Nkv;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       kf[ks] = ok ? *reinterpret_cast<const s16x8*>(kp + (size_t)kj * D + 16 * ks + 8 * g) : (s16x8){};
-      if constexpr (VFP8) {
-        const uint8_t* vp = (const uint8_t*)a.v + (size_t)bh * Nkv * D;
-        const float* vsc = a.v_scale + (size_t)bh * D + 16 * ks + 8 * g;
-        if (ok) {
+      vf[ks] = (s16x8){};
+      if (dk_wave && ok) {
+        if constexpr (VFP8) {
+          const uint8_t* vp = (const uint8_t*)a.v + (size_t)bh * Nkv * D;
+          const float* vsc = a.v_scale + (size_t)bh * D + 16 * ks + 8 * g;
           const u32x2 codes = *reinterpret_cast<const u32x2*>(vp + (size_t)kj * D + 16 * ks + 8 * g);
           uint32_t wv[4];
 #pragma unroll
@@ -364,22 +373,17 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
           }
           vf[ks] = __builtin_bit_cast(s16x8, (u32x4){wv[0], wv[1], wv[2], wv[3]});
         } else {
-          vf[ks] = (s16x8){};
+          const uint16_t* vp = (const uint16_t*)a.v + (size_t)bh * Nkv * D;
+          vf[ks] = *reinterpret_cast<const s16x8*>(vp + (size_t)kj * D + 16 * ks + 8 * g);
         }
-      } else {
-        const uint16_t* vp = (const uint16_t*)a.v + (size_t)bh * Nkv * D;
-        vf[ks] = ok ? *reinterpret_cast<const s16x8*>(vp + (size_t)kj * D + 16 * ks + 8 * g) : (s16x8){};
       }
     }
   }
   const float sk_lane = QKS ? (kj < Nkv ? a.k_scale[(size_t)bh * Nkv + kj] : 0.0f) : 1.0f;
 
-  f32x16 dk_acc[NDB], dv_acc[NDB];
+  f32x16 acc[NDB];   // dV^T (dV waves) or dK^T (dK waves)
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    dk_acc[db] = (f32x16){};
-    dv_acc[db] = (f32x16){};
-  }
+  for (int db = 0; db < NDB; ++db) acc[db] = (f32x16){};
 
   // Q and dO tiles go HBM -> LDS directly (double-buffered); the per-query
   // vectors (log2-domain LSE, Delta, Q scales, P-quant scales of this
@@ -387,8 +391,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   float vec0 = 0.0f, vec1 = 0.0f, vec2 = 0.0f;
   auto issue_tile = [&](int t, int buf) {
     const int qt0 = t * DKV_BQ;
-    tile_to_lds_async<D, DKV_BQ, 4>(qt_s[buf], qp, qt0, Nq, w, lane);
-    tile_to_lds_async<D, DKV_BQ, 4>(dot_s[buf], dop, qt0, Nq, w, lane);
+    tile_to_lds_async<D, DKV_BQ, 8>(qt_s[buf], qp, qt0, Nq, w, lane);
+    tile_to_lds_async<D, DKV_BQ, 8>(dot_s[buf], dop, qt0, Nq, w, lane);
     if (tid < DKV_BQ) {
       const int q = qt0 + tid;
       vec0 = q < Nq ? a.lse[(size_t)bh * Nq + q] * LOG2E : 0.0f;
@@ -431,80 +435,98 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     const int buf = t & 1;
     if (t + 1 < ntq) issue_tile(t + 1, buf ^ 1);
     if (wave_live) {
-    const char* Qt = qt_s[buf];
-    const char* dOt = dot_s[buf];
+      const char* Qt = qt_s[buf];
+      const char* dOt = dot_s[buf];
 #pragma unroll
-    for (int qb2 = 0; qb2 < DKV_BQ / 32; ++qb2) {
-      const int qs = qt0 + qb2 * 32;          // first query of this 32-block
-      if (qs >= Nq) break;
-      if (CAUSAL && qs + 31 < k0w) continue;  // every key of the wave is after every query
-      // ---- S = Q K^T, dP = dO V^T (lane: key kj, registers: 16 queries)
-      f32x16 s = (f32x16){}, dp = (f32x16){};
+      for (int qb2 = 0; qb2 < DKV_BQ / 32; ++qb2) {
+        const int qs = qt0 + qb2 * 32;          // first query of this 32-block
+        if (qs >= Nq) break;
+        if (CAUSAL && qs + 31 < k0w) continue;  // every key of the wave is after every query
+        // ---- S = Q K^T (lane: key kj, registers: 16 queries)
+        f32x16 sacc = (f32x16){};
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        s = DT::mfma(lds_row8<D>(Qt, qb2 * 32 + l32, 2 * ks + g), kf[ks], s);
-        dp = DT::mfma(lds_row8<D>(dOt, qb2 * 32 + l32, 2 * ks + g), vf[ks], dp);
-      }
-      const bool need_mask = (qs + 32 > Nq) || (k0w + 32 > Nkv) || (CAUSAL && qs < k0w + 31);
-      float p[16], pq[16], dsv[16];
+        for (int ks = 0; ks < NKS; ++ks) sacc = DT::mfma(lds_row8<D>(Qt, qb2 * 32 + l32, 2 * ks + g), kf[ks], sacc);
+        const bool need_mask = (qs + 32 > Nq) || (k0w + 32 > Nkv) || (CAUSAL && qs < k0w + 31);
+        // ---- P = exp2(S c - M), formed exactly as in the dQ kernel
+        float p[16];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int ql = qb2 * 32 + 8 * u + 4 * g;   // local query index of registers 4u..4u+3
-        const f32x4 mv = *reinterpret_cast<const f32x4*>(&m_s[buf][ql]);
-        const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&d_s[buf][ql]);
-        f32x4 sv = {0, 0, 0, 0}, rv = {0, 0, 0, 0};
-        if constexpr (PQ >= 0) {
-          sv = *reinterpret_cast<const f32x4*>(&qs_s[buf][mygrp][ql]);
-          rv = *reinterpret_cast<const f32x4*>(&qr_s[buf][mygrp][ql]);
-        }
-        f32x4 sq4 = {1.0f, 1.0f, 1.0f, 1.0f};
-        if constexpr (QKS) sq4 = *reinterpret_cast<const f32x4*>(&sq_s[buf][ql]);
+        for (int u = 0; u < 4; ++u) {
+          const int ql = qb2 * 32 + 8 * u + 4 * g;   // local query of registers 4u..4u+3
+          const f32x4 mv = *reinterpret_cast<const f32x4*>(&m_s[buf][ql]);
+          f32x4 sq4 = {1.0f, 1.0f, 1.0f, 1.0f};
+          if constexpr (QKS) sq4 = *reinterpret_cast<const f32x4*>(&sq_s[buf][ql]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * u + e;
-          // S and the log2 scale are formed exactly as in the dQ kernel
-          const float sr = QKS ? s[r] * sk_lane : s[r];
-          const float cr = QKS ? a.c * sq4[e] : a.c;
-          float x = fast_exp2(__builtin_fmaf(sr, cr, -mv[e]));
-          if (need_mask) {
-            const int q = qt0 + ql + e;
-            if (q >= Nq || kj >= Nkv || (CAUSAL && kj > q)) x = 0.0f;
-          }
-          p[r] = x;
-          dsv[r] = x * (dp[r] - dv4[e]);
-          if constexpr (QKS) dsv[r] *= sq4[e];   // dK = sm_scale sum_i dS_ij s_q[i] code_q[i]
-        }
-        if constexpr (PQ >= 0) {
-          // registers 4u+e hold different query rows: one (s, r) pair each
-#pragma unroll
-          for (int e = 0; e < 4; e += 2) {
+          for (int e = 0; e < 4; ++e) {
             const int r = 4 * u + e;
-            const f32x2 xq = fq_pair2<(PQ >= 0 ? PQ : 0)>(p[r], p[r + 1], FqScale{sv[e], rv[e]},
-                                                         FqScale{sv[e + 1], rv[e + 1]});
-            pq[r] = xq[0];
-            pq[r + 1] = xq[1];
+            const float sr = QKS ? sacc[r] * sk_lane : sacc[r];
+            const float cr = QKS ? a.c * sq4[e] : a.c;
+            p[r] = fast_exp2(__builtin_fmaf(sr, cr, -mv[e]));
+          }
+        }
+        if (need_mask) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int q = qs + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (q >= Nq || kj >= Nkv || (CAUSAL && kj > q)) p[r] = 0.0f;
+          }
+        }
+        if (!dk_wave) {
+          // ---- dV waves: P^ = FQ(P) per (query, 64-key group); dV^T += dO^T P^
+          uint32_t wp[8];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int ql = qb2 * 32 + 8 * u + 4 * g;
+            if constexpr (PQ >= 0) {
+              const f32x4 sv = *reinterpret_cast<const f32x4*>(&qs_s[buf][mygrp][ql]);
+              const f32x4 rv = *reinterpret_cast<const f32x4*>(&qr_s[buf][mygrp][ql]);
+#pragma unroll
+              for (int e = 0; e < 4; e += 2) {
+                const f32x2 xq = fq_pair2<(PQ >= 0 ? PQ : 0)>(p[4 * u + e], p[4 * u + e + 1], FqScale{sv[e], rv[e]},
+                                                             FqScale{sv[e + 1], rv[e + 1]});
+                wp[2 * u + e / 2] = DT::pack2(xq[0], xq[1]);
+              }
+            } else {
+              wp[2 * u] = DT::pack2(p[4 * u], p[4 * u + 1]);
+              wp[2 * u + 1] = DT::pack2(p[4 * u + 2], p[4 * u + 3]);
+            }
+          }
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const s16x8 p_op = __builtin_bit_cast(s16x8, (u32x4){wp[4 * h], wp[4 * h + 1], wp[4 * h + 2], wp[4 * h + 3]});
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+              acc[db] = DT::mfma(lds_tr8<D>(dOt, qb2 * 32 + 16 * h, db * 32, lane), p_op, acc[db]);
+          }
+        } else {
+          // ---- dK waves: dP = dO V^T, dS = P o (dP - Delta); dK^T += Q^T dS
+          f32x16 dp = (f32x16){};
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) dp = DT::mfma(lds_row8<D>(dOt, qb2 * 32 + l32, 2 * ks + g), vf[ks], dp);
+          uint32_t wd[8];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int ql = qb2 * 32 + 8 * u + 4 * g;
+            const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&d_s[buf][ql]);
+            f32x4 sq4 = {1.0f, 1.0f, 1.0f, 1.0f};
+            if constexpr (QKS) sq4 = *reinterpret_cast<const f32x4*>(&sq_s[buf][ql]);
+            float dsv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              dsv[e] = p[4 * u + e] * (dp[4 * u + e] - dv4[e]);
+              if constexpr (QKS) dsv[e] *= sq4[e];   // dK = sm_scale sum_i dS_ij s_q[i] code_q[i]
+            }
+            wd[2 * u] = DT::pack2(dsv[0], dsv[1]);
+            wd[2 * u + 1] = DT::pack2(dsv[2], dsv[3]);
+          }
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const s16x8 ds_op = __builtin_bit_cast(s16x8, (u32x4){wd[4 * h], wd[4 * h + 1], wd[4 * h + 2], wd[4 * h + 3]});
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+              acc[db] = DT::mfma(lds_tr8<D>(Qt, qb2 * 32 + 16 * h, db * 32, lane), ds_op, acc[db]);
           }
         }
       }
-      // ---- dV^T += dO^T P^,  dK^T += Q^T dS  (two 16-query k steps)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint32_t wp[4], wd[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int r0 = 8 * h + 2 * jj;
-          wp[jj] = (PQ >= 0) ? DT::pack2(pq[r0], pq[r0 + 1]) : DT::pack2(p[r0], p[r0 + 1]);
-          wd[jj] = DT::pack2(dsv[r0], dsv[r0 + 1]);
-        }
-        const s16x8 p_op = __builtin_bit_cast(s16x8, (u32x4){wp[0], wp[1], wp[2], wp[3]});
-        const s16x8 ds_op = __builtin_bit_cast(s16x8, (u32x4){wd[0], wd[1], wd[2], wd[3]});
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          dv_acc[db] = DT::mfma(lds_tr8<D>(dOt, qb2 * 32 + 16 * h, db * 32, lane), p_op, dv_acc[db]);
-          dk_acc[db] = DT::mfma(lds_tr8<D>(Qt, qb2 * 32 + 16 * h, db * 32, lane), ds_op, dk_acc[db]);
-        }
-      }
-    }
     }
     wait_vmem();
     if (t + 1 < ntq) finish_tile(buf ^ 1);
@@ -512,18 +534,16 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   }
 
   if (kj >= Nkv) return;
-  uint16_t* dkp = (uint16_t*)a.dk + (size_t)bh * Nkv * D;
-  uint16_t* dvp = (uint16_t*)a.dv + (size_t)bh * Nkv * D;
+  uint16_t* outp = (uint16_t*)(dk_wave ? a.dk : a.dv) + (size_t)bh * Nkv * D;
+  const float scale = dk_wave ? a.sm_scale : 1.0f;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int d = db * 32 + 8 * u + 4 * g;
-      const float x[4] = {dk_acc[db][4 * u], dk_acc[db][4 * u + 1], dk_acc[db][4 * u + 2], dk_acc[db][4 * u + 3]};
-      const float y[4] = {dv_acc[db][4 * u], dv_acc[db][4 * u + 1], dv_acc[db][4 * u + 2], dv_acc[db][4 * u + 3]};
-      *reinterpret_cast<u32x2*>(dkp + (size_t)kj * D + d) =
-          (u32x2){DT::pack2(x[0] * a.sm_scale, x[1] * a.sm_scale), DT::pack2(x[2] * a.sm_scale, x[3] * a.sm_scale)};
-      *reinterpret_cast<u32x2*>(dvp + (size_t)kj * D + d) = (u32x2){DT::pack2(y[0], y[1]), DT::pack2(y[2], y[3])};
+      const float x[4] = {acc[db][4 * u] * scale, acc[db][4 * u + 1] * scale, acc[db][4 * u + 2] * scale,
+                          acc[db][4 * u + 3] * scale};
+      *reinterpret_cast<u32x2*>(outp + (size_t)kj * D + d) = (u32x2){DT::pack2(x[0], x[1]), DT::pack2(x[2], x[3])};
     }
 }
 
@@ -537,7 +557,7 @@ struct DqK {
 template <class DT, int D, bool CAUSAL, int PQ, int IN>
 struct DkvK {
   static void run(dim3 g, const BwdArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((dkdv_kernel<DT, D, CAUSAL, PQ, IN>), g, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((dkdv_kernel<DT, D, CAUSAL, PQ, IN>), g, dim3(512), 0, st, a);
   }
 };
 
