@@ -38,11 +38,99 @@ def parse():
     ap.add_argument("--workload", default="dit_image")
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the oracle sample (0: skip)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (calibrates HBM byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a --copy-mib run "
+                         "into profiles/hbm_traffic_<workload>.json and exit (no GPU needed)")
     return ap.parse_args()
+
+
+KERNEL_TAGS = ("fwd_kernel", "delta_kernel", "dq_kernel", "dkdv_kernel", "token_quant_kernel")
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, copy_mib: int):
+    """Per-launch HBM bytes of each kernel from FETCH_SIZE / WRITE_SIZE (KiB
+    per dispatch), each scaled by what the same counter reads for the plain
+    copy of copy_mib MiB in the same run (known: copy_mib MiB read and
+    written)."""
+    import csv
+    from collections import defaultdict
+
+    def load(path, counter):
+        per = defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            tag = next((t for t in KERNEL_TAGS if f"qat::{t}<" in name), None)
+            if "copyBuffer" in name:
+                tag = "copy"
+            if tag:
+                per[tag].append(float(r["Counter_Value"]) * 1024.0)
+        return {t: sum(v) / len(v) for t, v in per.items()}
+
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    known = float(copy_mib << 20)
+    ff, wf = known / fetch["copy"], known / write["copy"]
+    from quantization_aware_attention_amd import workloads as W
+    w = W.WORKLOADS[workload]
+    e = 2  # bytes per element
+    BH = w.B * w.H
+    alg = {
+        "fwd_kernel": BH * (w.Nq + 2 * w.Nkv) * w.D * e + BH * w.Nq * (2 * w.D * e + 4),
+        "delta_kernel": BH * w.Nq * (2 * w.D * e + 4),
+        "dq_kernel": BH * (2 * w.Nq * w.D * e + 2 * w.Nkv * w.D * e + 8 * w.Nq) + BH * w.Nq * w.D * e,
+        "dkdv_kernel": BH * (2 * w.Nq * w.D * e + 2 * w.Nkv * w.D * e + 8 * w.Nq) + 2 * BH * w.Nkv * w.D * e,
+    }
+    out = {"workload": workload, "source_hash": kernel_source_hash(),
+           "calibration": {"copy_bytes": known, "fetch_counter_bytes": fetch["copy"],
+                           "write_counter_bytes": write["copy"], "fetch_factor": ff, "write_factor": wf},
+           "kernels": {}}
+    for t in fetch:
+        if t == "copy" or t not in write:
+            continue
+        fb, wb = fetch[t] * ff, write[t] * wf
+        out["kernels"][t] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb),
+                             "algorithmic_bytes": alg.get(t)}
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"hbm_traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources; HBM counter readings are valid only for the
+    kernels they were taken on."""
+    import hashlib
+    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "quantization_aware_attention_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(root)):
+        if name.endswith((".hip", ".hpp", ".cpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(root, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/hbm_traffic_<workload>.json), or None when the summary is
+    missing or was taken on different kernel sources."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_traffic_dit_image.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
 
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.copy_mib or 512)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the kernel runs on one "
               "GPU's share of the heads); run with --gpus 1", file=sys.stderr)
@@ -130,8 +218,16 @@ def main():
     dom = max((n for n in kernels if kernels[n][1] is not None), key=lambda n: kernel_ms[n])
     dom_tflops = kernels[dom][1] / (kernel_ms[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(dom_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": dom,
+                "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(dom), "kernel": dom,
                 "kernel_ms": {n: round(t, 4) for n, t in kernel_ms.items()}}
+
+    # ---- plain copy of a known size (counter calibration runs)
+    if args.copy_mib > 0:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
     # ---- float64 oracle on a bounded sample of the same workload
     cpu = None
@@ -176,6 +272,7 @@ def main():
                    "fa_convention_tflops": round(fa_conv, 2)},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)
 

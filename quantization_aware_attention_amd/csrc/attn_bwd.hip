@@ -145,8 +145,10 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float ks_s[2][DQ_BN];     // IN_QKS: key scales
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
-  const int bh = blockIdx.y;
-  const int qb = blockIdx.x * DQ_BM;
+  const int ntq = (a.Nq + DQ_BM - 1) / DQ_BM;
+  const int unit = xcd_unit(blockIdx.x, gridDim.x);
+  const int bh = unit / ntq;
+  const int qb = (CAUSAL ? ntq - 1 - unit % ntq : unit % ntq) * DQ_BM;
   const int q0 = qb + w * 32;
   const int qi = q0 + l32;
   const int Nq = a.Nq, Nkv = a.Nkv;
@@ -340,8 +342,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const bool dk_wave = w >= 4;
   const int kw = w & 3;
-  const int bh = blockIdx.y;
-  const int k0 = blockIdx.x * DKV_BN;
+  const int nkb = (a.Nkv + DKV_BN - 1) / DKV_BN;
+  const int unit = xcd_unit(blockIdx.x, gridDim.x);
+  const int bh = unit / nkb;
+  const int k0 = (unit % nkb) * DKV_BN;   // causal: key block 0 sees every query: longest first
   const int k0w = k0 + kw * 32;
   const int kj = k0w + l32;
   const int Nq = a.Nq, Nkv = a.Nkv;
@@ -479,12 +483,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdArgs a) {
             if constexpr (PQ >= 0) {
               const f32x4 sv = *reinterpret_cast<const f32x4*>(&qs_s[buf][mygrp][ql]);
               const f32x4 rv = *reinterpret_cast<const f32x4*>(&qr_s[buf][mygrp][ql]);
-#pragma unroll
-              for (int e = 0; e < 4; e += 2) {
-                const f32x2 xq = fq_pair2<(PQ >= 0 ? PQ : 0)>(p[4 * u + e], p[4 * u + e + 1], FqScale{sv[e], rv[e]},
-                                                             FqScale{sv[e + 1], rv[e + 1]});
-                wp[2 * u + e / 2] = DT::pack2(xq[0], xq[1]);
-              }
+              const FqScale f4[4] = {{sv[0], rv[0]}, {sv[1], rv[1]}, {sv[2], rv[2]}, {sv[3], rv[3]}};
+              const f32x4 xq = fq_quad<(PQ >= 0 ? PQ : 0)>(&p[4 * u], f4);
+              wp[2 * u] = DT::pack2(xq[0], xq[1]);
+              wp[2 * u + 1] = DT::pack2(xq[2], xq[3]);
             } else {
               wp[2 * u] = DT::pack2(p[4 * u], p[4 * u + 1]);
               wp[2 * u + 1] = DT::pack2(p[4 * u + 2], p[4 * u + 3]);
@@ -615,7 +617,7 @@ hipError_t launch_bwd_dq(const Shape& s, const Inputs& in, const void* dout, con
   BwdArgs a = make_args(s, in, dout, lse, delta, sm_scale);
   a.dq = dq;
   a.p_amax = p_amax;
-  dim3 grid((s.Nq + DQ_BM - 1) / DQ_BM, s.B * s.H);
+  dim3 grid(((s.Nq + DQ_BM - 1) / DQ_BM) * s.B * s.H);
   return pick_all<DqK>(s, grid, a, causal, pfmt, in.mode, st);
 }
 
@@ -626,7 +628,7 @@ hipError_t launch_bwd_dkdv(const Shape& s, const Inputs& in, const void* dout, c
   a.p_amax_in = p_amax;
   a.dk = dk;
   a.dv = dv;
-  dim3 grid((s.Nkv + DKV_BN - 1) / DKV_BN, s.B * s.H);
+  dim3 grid(((s.Nkv + DKV_BN - 1) / DKV_BN) * s.B * s.H);
   return pick_all<DkvK>(s, grid, a, causal, pfmt, in.mode, st);
 }
 

@@ -58,8 +58,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) float ks_s[2][FWD_BN];   // IN_QKS: key scales of the tile
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
-  const int bh = blockIdx.y;
-  const int qb = blockIdx.x * FWD_BM;
+  const int ntq = (a.Nq + FWD_BM - 1) / FWD_BM;
+  const int unit = xcd_unit(blockIdx.x, gridDim.x);
+  const int bh = unit / ntq;
+  // causal: the longest rows first, so short tiles fill the tail of the launch
+  const int qb = (CAUSAL ? ntq - 1 - unit % ntq : unit % ntq) * FWD_BM;
   const int q0 = qb + w * 32;
   const int qi = q0 + l32;
   const int Nq = a.Nq, Nkv = a.Nkv;
@@ -225,12 +228,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         const int kb = kk >> 1, h = kk & 1;
         uint32_t ph[4], pq[4];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const float x0 = p[kb][8 * h + 2 * jj], x1 = p[kb][8 * h + 2 * jj + 1];
-          ph[jj] = DT::pack2(x0, x1);
-          if constexpr (PQ >= 0) {
-            const f32x2 xq = fq_pair<(PQ >= 0 ? PQ : 0)>(x0, x1, fs);
-            pq[jj] = DT::pack2(xq[0], xq[1]);
+        for (int jj = 0; jj < 4; ++jj) ph[jj] = DT::pack2(p[kb][8 * h + 2 * jj], p[kb][8 * h + 2 * jj + 1]);
+        if constexpr (PQ >= 0) {
+          const FqScale f4[4] = {fs, fs, fs, fs};
+#pragma unroll
+          for (int jq = 0; jq < 2; ++jq) {
+            const f32x4 xq = fq_quad<(PQ >= 0 ? PQ : 0)>(&p[kb][8 * h + 4 * jq], f4);
+            pq[2 * jq] = DT::pack2(xq[0], xq[1]);
+            pq[2 * jq + 1] = DT::pack2(xq[2], xq[3]);
           }
         }
         const s16x8 bh_op = __builtin_bit_cast(s16x8, (u32x4){ph[0], ph[1], ph[2], ph[3]});
@@ -281,7 +286,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
 template <class DT, int D, bool CAUSAL, int PQ, int IN>
 static hipError_t fwd_launch(const Shape& s, const FwdArgs& a, hipStream_t st) {
-  dim3 grid((s.Nq + FWD_BM - 1) / FWD_BM, s.B * s.H);
+  dim3 grid(((s.Nq + FWD_BM - 1) / FWD_BM) * s.B * s.H);
   hipLaunchKernelGGL((fwd_kernel<DT, D, CAUSAL, PQ, IN>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }

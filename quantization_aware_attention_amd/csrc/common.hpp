@@ -198,6 +198,42 @@ __device__ __forceinline__ f32x2 fq_pair(float x0, float x1, FqScale q, uint32_t
   return fq_pair2<FMT>(x0, x1, q, q, codes);
 }
 
+// Four values, each with its own scale pair: the four codes share one dword
+// (low word first), so no register clearing or masking is needed.
+template <int FMT>
+__device__ __forceinline__ f32x4 fq_quad(const float x[4], const FqScale q[4]) {
+  int pk;
+  if constexpr (FMT == 0) {
+    pk = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] * q[0].r, x[1] * q[1].r, __builtin_bit_cast(int, x[0]), false);
+    pk = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] * q[2].r, x[3] * q[3].r, pk, true);
+  } else {
+    pk = __builtin_amdgcn_cvt_pk_bf8_f32(x[0] * q[0].r, x[1] * q[1].r, __builtin_bit_cast(int, x[0]), false);
+    pk = __builtin_amdgcn_cvt_pk_bf8_f32(x[2] * q[2].r, x[3] * q[3].r, pk, true);
+  }
+  f32x2 lo, hi;
+  if constexpr (FMT == 0) {
+    lo = __builtin_amdgcn_cvt_pk_f32_fp8(pk, false);
+    hi = __builtin_amdgcn_cvt_pk_f32_fp8(pk, true);
+  } else {
+    lo = __builtin_amdgcn_cvt_pk_f32_bf8(pk, false);
+    hi = __builtin_amdgcn_cvt_pk_f32_bf8(pk, true);
+  }
+  return (f32x4){lo[0] * q[0].s, lo[1] * q[1].s, hi[0] * q[2].s, hi[1] * q[3].s};
+}
+
+// ---------------------------------------------------------------- work order
+// MI355X deals the workgroups of a launch to its 8 XCDs round-robin by linear
+// id, and each XCD has its own L2.  xcd_unit() renumbers the launch so that
+// every XCD receives one contiguous range of work units: the tiles of one
+// (batch, head) then run on the same XCD and share its L2 for the K/V (or
+// Q/dO) tiles they all stream.  Bijective on [0, total).
+constexpr int NUM_XCD = 8;
+__device__ __forceinline__ int xcd_unit(int linear, int total) {
+  const int x = linear % NUM_XCD, idx = linear / NUM_XCD;
+  const int base = total / NUM_XCD, rem = total % NUM_XCD;
+  return x * base + min(x, rem) + idx;
+}
+
 // ---------------------------------------------------------------- misc
 __device__ __forceinline__ float shfl_xor32(float x) {
   return __shfl_xor(x, 32, 64);
