@@ -169,6 +169,18 @@ int qat_quant_v_fp8(const qat_attn_dims* dims, const void* v, uint8_t* codes, fl
 int qat_fake_quant_rows(const float* x, int32_t rows, int32_t cols, int32_t group, int32_t fmt,
                         uint8_t* codes, float* scales, float* xhat, void* stream);
 
+/*
+ * Self-test of a hardware property the kernels rely on.  The forward takes a
+ * row's P-quant absmax as exp2 of the row group's largest argument rather
+ * than as the max over the exp2 results; both are the same value exactly when
+ * the exp2 instruction (v_exp_f32) never decreases between adjacent fp32
+ * arguments.  Counts the adjacent fp32 pairs x < x' in [lo, hi] with
+ * exp2(x') < exp2(x) into *violations (a device uint32, overwritten), over
+ * every fp32 value in the range.  Errors: QAT_EINVAL (null pointer, NaN
+ * bound, lo > hi), QAT_EHIP.
+ */
+int qat_selftest_exp2_monotone(float lo, float hi, uint32_t* violations, void* stream);
+
 /* QAT_ATTN_P_GROUP as compiled into the kernels. */
 int qat_attn_p_group(void);
 

@@ -217,6 +217,12 @@ int qat_fake_quant_rows(const float* x, int32_t rows, int32_t cols, int32_t grou
   return QAT_OK;
 }
 
+int qat_selftest_exp2_monotone(float lo, float hi, uint32_t* violations, void* stream) {
+  if (!violations || !(lo <= hi) || std::isnan(lo) || std::isnan(hi)) return QAT_EINVAL;
+  QAT_TRY(qat::launch_exp2_selftest(lo, hi, violations, static_cast<hipStream_t>(stream)));
+  return QAT_OK;
+}
+
 int qat_attn_p_group(void) { return QAT_ATTN_P_GROUP; }
 
 const char* qat_attn_strerror(int status) {

@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2][2][TILE];   // [buffer][K, V]
   __shared__ __attribute__((aligned(16))) float ks_s[2][DQ_BN];     // IN_QKS: key scales
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int ntq = (a.Nq + DQ_BM - 1) / DQ_BM;
   const int unit = xcd_unit(blockIdx.x, gridDim.x);
   const int bh = unit / ntq;
@@ -178,8 +178,10 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   // V codes and key scales take a register detour.
   u32x2 vcode[LPT];
   float ksreg = 0.0f;
+  TileCopy<D, DQ_BN, 4> copy;
+  copy.init(w, lane);
   auto issue_tile = [&](int t, int buf) {
-    tile_to_lds_async<D, DQ_BN, 4>(smem[buf][0], kp, t * DQ_BN, Nkv, w, lane);
+    copy.issue(smem[buf][0], kp, t * DQ_BN, Nkv);
     if constexpr (VFP8) {
 #pragma unroll
       for (int u = 0; u < LPT; ++u) {
@@ -188,7 +190,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
         vcode[u] = *reinterpret_cast<const u32x2*>(vp + (size_t)key * D + ch * 8);
       }
     } else {
-      tile_to_lds_async<D, DQ_BN, 4>(smem[buf][1], (const uint16_t*)vp, t * DQ_BN, Nkv, w, lane);
+      copy.issue(smem[buf][1], (const uint16_t*)vp, t * DQ_BN, Nkv);
     }
     if constexpr (QKS) {
       const int key = t * DQ_BN + tid;
@@ -395,8 +397,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdArgs a) {
   float vec0 = 0.0f, vec1 = 0.0f, vec2 = 0.0f;
   auto issue_tile = [&](int t, int buf) {
     const int qt0 = t * DKV_BQ;
-    tile_to_lds_async<D, DKV_BQ, 8>(qt_s[buf], qp, qt0, Nq, w, lane);
-    tile_to_lds_async<D, DKV_BQ, 8>(dot_s[buf], dop, qt0, Nq, w, lane);
+    TileCopy<D, DKV_BQ, 8> copy;   // offsets recomputed per tile: registers are tight here
+    copy.init(wave_id(), lane);
+    copy.issue(qt_s[buf], qp, qt0, Nq);
+    copy.issue(dot_s[buf], dop, qt0, Nq);
     if (tid < DKV_BQ) {
       const int q = qt0 + tid;
       vec0 = q < Nq ? a.lse[(size_t)bh * Nq + q] * LOG2E : 0.0f;

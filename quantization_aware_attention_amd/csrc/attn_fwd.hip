@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2][2][TILE];
   __shared__ __attribute__((aligned(16))) float ks_s[2][FWD_BN];   // IN_QKS: key scales of the tile
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int ntq = (a.Nq + FWD_BM - 1) / FWD_BM;
   const int unit = xcd_unit(blockIdx.x, gridDim.x);
   const int bh = unit / ntq;
@@ -90,8 +90,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   // way into LDS); every other tile goes HBM -> LDS directly.
   u32x2 vcode[LPT];
   float ksreg = 0.0f;
+  TileCopy<D, FWD_BN, 4> copy;
+  copy.init(w, lane);
   auto issue_tile = [&](int t, int buf) {
-    tile_to_lds_async<D, FWD_BN, 4>(smem[buf][0], kp, t * FWD_BN, Nkv, w, lane);
+    copy.issue(smem[buf][0], kp, t * FWD_BN, Nkv);
     if constexpr (VFP8) {
 #pragma unroll
       for (int u = 0; u < LPT; ++u) {
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         vcode[u] = *reinterpret_cast<const u32x2*>(vp8 + (size_t)key * D + ch * 8);
       }
     } else {
-      tile_to_lds_async<D, FWD_BN, 4>(smem[buf][1], (const uint16_t*)vp8, t * FWD_BN, Nkv, w, lane);
+      copy.issue(smem[buf][1], (const uint16_t*)vp8, t * FWD_BN, Nkv);
     }
     if constexpr (QKS) {
       const int key = t * FWD_BN + tid;
@@ -205,23 +207,24 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         m_used = m_new;
       }
       const float m_sub = (m_used == -INFINITY) ? 0.0f : m_used;
+      // ---- P-quant scale of this row's 64-key group: the absmax of p is
+      // exp2 of the largest argument (exp2 is monotone; mx is the row max)
+      FqScale fs = {0.0f, 0.0f};
+      if constexpr (PQ >= 0) {
+        const float pmax = (mx == -INFINITY) ? 0.0f : fast_exp2(__builtin_fmaf(mx, c_row, -m_sub));
+        fs = fq_scale(pmax, Fp8Fmt<(PQ >= 0 ? PQ : 0)>::FMAX);
+      }
       // ---- p = exp2(S*c - m)
       float p[2][16];
-      float psum = 0.0f, pmax = 0.0f;
+      float psum = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           p[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c_row, -m_sub));
           psum += p[kb][r];
-          pmax = fmaxf(pmax, p[kb][r]);
         }
       l_part += psum;
-      FqScale fs = {0.0f, 0.0f};
-      if constexpr (PQ >= 0) {
-        pmax = fmaxf(pmax, shfl_xor32(pmax));
-        fs = fq_scale(pmax, Fp8Fmt<(PQ >= 0 ? PQ : 0)>::FMAX);
-      }
       // ---- O^T += V^T P^T  (4 k-steps of 16 keys)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {

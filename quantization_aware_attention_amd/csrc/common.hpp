@@ -112,30 +112,52 @@ __device__ __forceinline__ s16x8 lds_tr8(const char* tile, int row0, int col0, i
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Asynchronous copy of one [BN x D] 16-bit tile from HBM into the swizzled LDS
+// Asynchronous copy of [BN x D] 16-bit tiles from HBM into the swizzled LDS
 // layout with global_load_lds_dwordx4: every wave instruction fills one
 // contiguous KiB of LDS (lane l -> bytes 16l..16l+15), so lane l fetches the
-// global chunk that belongs at that LDS position.  Rows past `nrows` are
-// clamped to the last valid row (finite data; the kernels mask those keys).
-// Each of the NW waves issues (BN*D*2/1024)/NW instructions.
+// global chunk that belongs at that LDS position.  The per-lane source
+// offsets are fixed for the whole loop; each copy only adds a wave-uniform
+// base.  Rows past `nrows` are clamped to the last valid row (finite data;
+// the kernels mask those rows).  Each of the NW waves issues
+// (BN*D*2/1024)/NW instructions.
 template <int D, int BN, int NW>
-__device__ __forceinline__ void tile_to_lds_async(char* lds_tile, const uint16_t* src, int row0, int nrows,
-                                                  int wave, int lane) {
-  constexpr int ROW_BYTES = D * 2;
-  constexpr int CPR = ROW_BYTES / 16;                 // chunks per row
-  constexpr int ROWS_PER_KIB = 1024 / ROW_BYTES;
-  constexpr int KIB = BN * ROW_BYTES / 1024;
+struct TileCopy {
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int CPR = ROW_BYTES / 16;                 // chunks per row
+  static constexpr int ROWS_PER_KIB = 1024 / ROW_BYTES;
+  static constexpr int KIB = BN * ROW_BYTES / 1024;
+  static constexpr int PER_WAVE = KIB / NW;
   static_assert(KIB % NW == 0, "tile must split evenly over the waves");
+  uint32_t off[PER_WAVE];   // byte offset of this lane's source chunk inside the tile
+  int wave;                 // wave index (uniform)
+
+  __device__ __forceinline__ void init(int wave_uniform, int lane) {
+    wave = wave_uniform;
 #pragma unroll
-  for (int u = 0; u < KIB / NW; ++u) {
-    const int blk = wave * (KIB / NW) + u;
-    const int row = blk * ROWS_PER_KIB + lane / CPR;
-    const int chunk = (lane % CPR) ^ swz<D>(row);
-    const int grow = min(row0 + row, nrows - 1);
-    const uint16_t* g = src + (size_t)grow * D + chunk * 8;
-    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(lds_tile + blk * 1024), 16, 0, 0);
+    for (int u = 0; u < PER_WAVE; ++u) {
+      const int blk = wave * PER_WAVE + u;
+      const int row = blk * ROWS_PER_KIB + lane / CPR;
+      const int chunk = (lane % CPR) ^ swz<D>(row);
+      off[u] = (uint32_t)(row * ROW_BYTES + chunk * 16);
+    }
   }
-}
+  // Copy rows [row0, row0 + BN) of src ([nrows x D]) into lds_tile.
+  __device__ __forceinline__ void issue(char* lds_tile, const uint16_t* src, int row0, int nrows) const {
+    const char* base = reinterpret_cast<const char*>(src + (size_t)row0 * D);
+    const bool full = row0 + BN <= nrows;
+#pragma unroll
+    for (int u = 0; u < PER_WAVE; ++u) {
+      uint32_t o = off[u];
+      if (!full) {   // tail tile: clamp the row, keep the column
+        const int row = (int)(o / ROW_BYTES);
+        const int r = min(row0 + row, nrows - 1) - row0;
+        o = (uint32_t)(r * ROW_BYTES) + (o % ROW_BYTES);
+      }
+      __builtin_amdgcn_global_load_lds((const void*)(base + o),
+                                       (lds_void*)(lds_tile + (wave * PER_WAVE + u) * 1024), 16, 0, 0);
+    }
+  }
+};
 
 // Wait for this wave's outstanding global loads (including LDS DMA).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
@@ -239,6 +261,13 @@ __device__ __forceinline__ float shfl_xor32(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// v_exp_f32.  The kernels take a row group's P absmax as exp2 of the largest
+// argument (instead of a max over the exp2 results); that is exact because
+// this instruction is monotone non-decreasing over every fp32 argument the
+// kernels can produce (checked exhaustively by qat_selftest_exp2_monotone).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Wave index as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 }  // namespace qat

@@ -45,6 +45,9 @@ hipError_t launch_v_quant(int dtype, int D, int BH, int N, const void* v, uint8_
 hipError_t launch_fq_rows(const float* x, int rows, int cols, int group, int fmt, uint8_t* codes,
                           float* scales, float* xhat, hipStream_t st);
 
+// Self-test: count decreasing adjacent pairs of v_exp_f32 over fp32 [lo, hi].
+hipError_t launch_exp2_selftest(float lo, float hi, uint32_t* violations, hipStream_t st);
+
 // Backward pieces.
 hipError_t launch_bwd_delta(const Shape& s, const void* o_hp, const void* dout, float* delta,
                             hipStream_t st);

@@ -163,4 +163,44 @@ hipError_t launch_fq_rows(const float* x, int rows, int cols, int group, int fmt
   return hipGetLastError();
 }
 
+// Self-test: count adjacent fp32 pairs x < y (in value order, within
+// [key_lo, key_hi] of the order-preserving integer key of fp32) whose
+// v_exp_f32 results decrease.  Each thread walks one contiguous run of keys.
+__device__ __forceinline__ float from_order_key(uint32_t k) {
+  const uint32_t bits = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __builtin_bit_cast(float, bits);
+}
+
+__global__ __launch_bounds__(256) void exp2_monotone_kernel(uint32_t key_lo, uint32_t key_hi, uint32_t per_thread,
+                                                            uint32_t* violations) {
+  const uint64_t start = (uint64_t)key_lo + ((uint64_t)blockIdx.x * 256 + threadIdx.x) * per_thread;
+  if (start >= key_hi) return;
+  const uint64_t stop = min((uint64_t)key_hi, start + per_thread);
+  uint32_t bad = 0;
+  float prev = fast_exp2(from_order_key((uint32_t)start));
+  for (uint64_t k = start + 1; k <= stop; ++k) {
+    const float cur = fast_exp2(from_order_key((uint32_t)k));
+    bad += cur < prev;
+    prev = cur;
+  }
+  if (bad) atomicAdd(violations, bad);
+}
+
+__global__ void zero_u32(uint32_t* p) { *p = 0; }
+
+hipError_t launch_exp2_selftest(float lo, float hi, uint32_t* violations, hipStream_t st) {
+  auto key = [](float f) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, f);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  };
+  const uint32_t klo = key(lo), khi = key(hi);
+  hipLaunchKernelGGL(zero_u32, dim3(1), dim3(1), 0, st, violations);
+  if (khi <= klo) return hipGetLastError();
+  const uint32_t per = 4096;
+  const uint64_t threads = ((uint64_t)khi - klo + per - 1) / per;
+  hipLaunchKernelGGL(exp2_monotone_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, klo, khi, per,
+                     violations);
+  return hipGetLastError();
+}
+
 }  // namespace qat

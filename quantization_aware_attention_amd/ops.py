@@ -73,6 +73,8 @@ def lib():
     L.qat_quant_v_fp8.restype = ctypes.c_int
     L.qat_fake_quant_rows.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp]
     L.qat_fake_quant_rows.restype = ctypes.c_int
+    L.qat_selftest_exp2_monotone.argtypes = [f32, f32, vp, vp]
+    L.qat_selftest_exp2_monotone.restype = ctypes.c_int
     L.qat_attn_p_group.argtypes = []
     L.qat_attn_p_group.restype = ctypes.c_int
     L.qat_attn_strerror.argtypes = [ctypes.c_int]
@@ -191,3 +193,12 @@ def fake_quant_rows(x, group, fmt):
     _check("qat_fake_quant_rows", lib().qat_fake_quant_rows(_ptr(x), rows, cols, group, fmt, _ptr(codes),
                                                             _ptr(scales), _ptr(xhat), _stream()))
     return codes, scales, xhat
+
+
+def selftest_exp2_monotone(lo=float("-inf"), hi=128.0) -> int:
+    """Number of adjacent fp32 pairs in [lo, hi] where the GPU's exp2 decreases."""
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    _check("qat_selftest_exp2_monotone",
+           lib().qat_selftest_exp2_monotone(float(lo), float(hi), _ptr(out), _stream()))
+    torch.cuda.synchronize()
+    return int(out.item())

@@ -109,3 +109,6 @@ def test_other_entry_points_validate(L):
     assert L.qat_quant_v_fp8(ctypes.byref(D(1, 1, 0, 16, 96, 0)), FAKE, FAKE, FAKE, None) == ops.QAT_EUNSUPPORTED
     assert L.qat_quant_v_fp8(ctypes.byref(D(1, 1, 0, 16, 64, 0)), None, FAKE, FAKE, None) == ops.QAT_EINVAL
     assert L.qat_quant_v_fp8(ctypes.byref(D(1, 1, 0, 0, 64, 0)), None, None, None, None) == ops.QAT_OK
+    assert L.qat_selftest_exp2_monotone(0.0, 1.0, None, None) == ops.QAT_EINVAL
+    assert L.qat_selftest_exp2_monotone(2.0, 1.0, FAKE, None) == ops.QAT_EINVAL
+    assert L.qat_selftest_exp2_monotone(float("nan"), 1.0, FAKE, None) == ops.QAT_EINVAL

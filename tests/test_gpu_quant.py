@@ -127,3 +127,11 @@ def test_v_quant_matches_oracle(N):
     c_ref, s_ref = oracle.quantize_v_channels(inp["v"], "e5m2")
     assert np.array_equal(codes.cpu().numpy(), c_ref)
     assert np.array_equal(vs.cpu().numpy(), s_ref)
+
+
+def test_exp2_is_monotone_over_all_fp32():
+    # The forward's P-quant absmax is exp2 of the row group's largest
+    # argument; that equals the max over exp2 values because the instruction
+    # never decreases.  Checked over every fp32 value from -inf to 128.
+    from quantization_aware_attention_amd import ops
+    assert ops.selftest_exp2_monotone(float("-inf"), 128.0) == 0
