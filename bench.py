@@ -46,7 +46,22 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_TAGS = ("fwd_kernel", "delta_kernel", "dq_kernel", "dkdv_kernel", "token_quant_kernel")
+# stage label -> kernels that implement it (the forward has a ping-pong kernel
+# for value inputs and a separate one for fp8 V)
+KERNEL_TAGS = {
+    "fwd_kernel": ("fwd_pp_kernel", "fwd_kernel"),
+    "delta_kernel": ("delta_kernel",),
+    "dq_kernel": ("dq_kernel",),
+    "dkdv_kernel": ("dkdv_kernel",),
+    "token_quant_kernel": ("token_quant_kernel",),
+}
+
+
+def stage_of(kernel_name: str):
+    for tag, names in KERNEL_TAGS.items():
+        if any(f"qat::{n}<" in kernel_name for n in names):
+            return tag
+    return None
 
 
 def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, copy_mib: int):
@@ -63,7 +78,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, copy_mib: int):
             if r["Counter_Name"] != counter:
                 continue
             name = r["Kernel_Name"]
-            tag = next((t for t in KERNEL_TAGS if f"qat::{t}<" in name), None)
+            tag = stage_of(name)
             if "copyBuffer" in name:
                 tag = "copy"
             if tag:

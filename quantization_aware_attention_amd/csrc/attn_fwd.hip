@@ -155,6 +155,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       const char* Kt = smem[buf][0];
       const char* Vt = smem[buf][1];
       // ---- S^T = K Q^T (two 32-key blocks)
+      prio_mfma();
       f32x16 s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -165,6 +166,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
           s[kb] = DT::mfma(ka, qf[ks], s[kb]);
         }
       }
+      prio_valu();
       if constexpr (QKS) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -287,10 +289,319 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong forward (values or per-token-scaled codes as inputs).
+//
+// Eight waves own 256 query rows (32 each); waves w and w+4 share a SIMD.
+// The waves form two groups that alternate between an MFMA phase
+// (P@V of the previous tile, then S^T of this tile) and a VALU phase
+// (masks, running maximum, exp2, P fake quant, operand packing), separated
+// by workgroup barriers: while one group keeps the SIMD's matrix core busy
+// the other works through its vector instructions.  Phase p:
+//   group 0: p = 2t   -> MFMA(t),   p = 2t+1 -> VALU(t)
+//   group 1: p = 2t+1 -> MFMA(t),   p = 2t+2 -> VALU(t)
+// with MFMA(T) = P@V of the last tile only.  K(t) is read in phases 2t and
+// 2t+1, V(t) in phases 2t+2 and 2t+3 (both double-buffered).  The block's Q
+// rows stay in LDS; the MFMA phase is one software-pipelined stream whose
+// LDS operands are read two steps ahead of their MFMAs.  Tile copies are
+// issued by group 0 in its VALU phases and waited for before the barrier,
+// so no MFMA phase ever waits on global memory.
+constexpr int PP_BM = 256;
+
+template <class DT, int D, bool CAUSAL, int PQ, int IN>
+__global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
+  static_assert(IN != IN_VFP8, "fp8 V uses fwd_kernel");
+  constexpr bool QKS = IN == IN_QKS;
+  constexpr int TILE = FWD_BN * D * 2;
+  constexpr int NDB = D / 32;
+  constexpr int NKS = D / 16;
+  constexpr int FQF = PQ >= 0 ? PQ : 0;
+  constexpr int NPV = 4 * NDB;   // P@V steps of an MFMA phase
+  constexpr int PP_AHEAD = 2;    // steps whose LDS operands are in flight
+  __shared__ __attribute__((aligned(16))) char kbuf[2][TILE];
+  __shared__ __attribute__((aligned(16))) char vbuf[2][TILE];
+  __shared__ __attribute__((aligned(16))) float ks_s[2][FWD_BN];   // IN_QKS: key scales of K(t)
+  __shared__ __attribute__((aligned(16))) char qbuf[PP_BM * D * 2];   // the block's Q rows
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int grp = w >> 2;
+  const int ntq = (a.Nq + PP_BM - 1) / PP_BM;
+  const int unit = xcd_unit(blockIdx.x, gridDim.x);
+  const int bh = unit / ntq;
+  const int qb = (CAUSAL ? ntq - 1 - unit % ntq : unit % ntq) * PP_BM;
+  const int q0 = qb + w * 32;
+  const int qi = q0 + l32;
+  const int Nq = a.Nq, Nkv = a.Nkv;
+  const uint16_t* qp = (const uint16_t*)a.q + (size_t)bh * Nq * D;
+  const uint16_t* kp = (const uint16_t*)a.k + (size_t)bh * Nkv * D;
+  const uint16_t* vp = (const uint16_t*)a.v + (size_t)bh * Nkv * D;
+
+  {   // Q rows [qb, qb + PP_BM) into LDS (rows past Nq repeat the last row)
+    TileCopy<D, PP_BM, 8> qcopy;
+    qcopy.init(wave_id(), lane);
+    qcopy.issue(qbuf, qp, qb, Nq);
+  }
+  // exponent scale of this row; a zero per-token Q scale (all-zero row, every
+  // score 0) is raised to the smallest normal so that masked scores stay -inf
+  float c_row = a.c;
+  if constexpr (QKS) c_row = a.c * fmaxf(qi < Nq ? a.q_scale[(size_t)bh * Nq + qi] : 1.0f, 1.17549435e-38f);
+  const float* ksp = QKS ? a.k_scale + (size_t)bh * Nkv : nullptr;
+
+  const int kv_end = CAUSAL ? min(Nkv, qb + PP_BM) : Nkv;
+  const int T = (kv_end + FWD_BN - 1) / FWD_BN;
+  TileCopy<D, FWD_BN, 4> copy;   // used by group 0 only
+  copy.init(wave_id() & 3, lane);
+  float ksreg = 0.0f;
+
+  float m_used = -INFINITY, l_part = 0.0f;
+  f32x16 o_acc[NDB], oh_acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    o_acc[db] = (f32x16){};
+    oh_acc[db] = (f32x16){};
+  }
+  // S^T of a tile from its MFMA phase to its VALU phase; the VALU phase then
+  // overwrites it in place with the packed operands of P@V: for k-step kk
+  // (keys 16kk..16kk+15) words s[kk/2][8(kk%2) + 0..3] hold P^ and
+  // words + 4..7 hold P_hp, until the next MFMA phase consumes them.
+  f32x16 s[2];
+  const bool live_rows = q0 < Nq;
+  auto active = [&](int t) { return live_rows && (!CAUSAL || t * FWD_BN <= q0 + 31); };
+
+  auto scale_keys = [&](int t) __attribute__((always_inline)) {   // IN_QKS: S^T *= per-key scales
+    if constexpr (QKS) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const f32x4 sk = *reinterpret_cast<const f32x4*>(&ks_s[t & 1][kb * 32 + 8 * u + 4 * g]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[kb][4 * u + e] *= sk[e];
+        }
+    }
+  };
+  // The MFMA phase as one stream of steps: NPV steps of P@V (one V fragment,
+  // the O and O_hp MFMAs of a 16-key by 32-column block) then NKS steps of
+  // S^T = K Q^T (a Q fragment and two K fragments, two MFMAs).  Step st
+  // reads the fragments of step st + PP_AHEAD; scheduling fences keep that
+  // order, so every MFMA finds its LDS operands already loaded.
+  struct Bundle { s16x8 a, b, c; };
+  auto fetch = [&](const char* Vt, const char* Kt, int st) __attribute__((always_inline)) {
+    Bundle r;
+    if (st < NPV) {
+      r.a = lds_tr8<D>(Vt, (st / NDB) * 16, (st % NDB) * 32, lane);
+    } else {
+      const int ks = st - NPV;
+      r.a = lds_row8<D>(qbuf, w * 32 + l32, 2 * ks + g);
+      r.b = lds_row8<D>(Kt, l32, 2 * ks + g);
+      r.c = lds_row8<D>(Kt, 32 + l32, 2 * ks + g);
+    }
+    return r;
+  };
+  auto step = [&](const Bundle& cur, int st) __attribute__((always_inline)) {
+    if (st < NPV) {   // O^T += V^T P^T, k-step kk, column block db
+      const int kk = st / NDB, db = st % NDB, kb = kk >> 1, o8 = 8 * (kk & 1);
+      const s16x8 bhp = __builtin_bit_cast(s16x8, (f32x4){s[kb][o8 + 4], s[kb][o8 + 5], s[kb][o8 + 6], s[kb][o8 + 7]});
+      if constexpr (PQ >= 0) {
+        const s16x8 bq = __builtin_bit_cast(s16x8, (f32x4){s[kb][o8], s[kb][o8 + 1], s[kb][o8 + 2], s[kb][o8 + 3]});
+        o_acc[db] = DT::mfma(cur.a, bq, o_acc[db]);
+        oh_acc[db] = DT::mfma(cur.a, bhp, oh_acc[db]);
+      } else {
+        o_acc[db] = DT::mfma(cur.a, bhp, o_acc[db]);
+      }
+    } else {          // S^T = K Q^T, k-step ks
+      if (st == NPV) {
+        s[0] = (f32x16){};
+        s[1] = (f32x16){};
+      }
+      s[0] = DT::mfma(cur.b, cur.a, s[0]);
+      s[1] = DT::mfma(cur.c, cur.a, s[1]);
+    }
+  };
+  auto mfma_phase = [&](int t) __attribute__((always_inline)) {
+    const bool do_pv = t >= 1 && active(t - 1);
+    const bool do_qk = t < T && active(t);
+    if (do_pv && do_qk) {
+      const char* Vt = vbuf[(t - 1) & 1];
+      const char* Kt = kbuf[t & 1];
+      Bundle ring[PP_AHEAD];
+#pragma unroll
+      for (int st = 0; st < PP_AHEAD; ++st) ring[st] = fetch(Vt, Kt, st);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int st = 0; st < NPV + NKS; ++st) {
+        const Bundle cur = ring[st % PP_AHEAD];
+        if (st + PP_AHEAD < NPV + NKS) ring[st % PP_AHEAD] = fetch(Vt, Kt, st + PP_AHEAD);
+        __builtin_amdgcn_sched_barrier(0);
+        step(cur, st);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      scale_keys(t);
+    } else {          // first and last phases, causal edges: the same steps unpipelined
+      const char* Vt = vbuf[(t - 1) & 1];
+      const char* Kt = kbuf[t & 1];
+      if (do_pv) {
+#pragma unroll
+        for (int st = 0; st < NPV; ++st) step(fetch(Vt, Kt, st), st);
+      }
+      if (do_qk) {
+#pragma unroll
+        for (int st = NPV; st < NPV + NKS; ++st) step(fetch(Vt, Kt, st), st);
+        scale_keys(t);
+      }
+    }
+  };
+  auto valu_phase = [&](int t) __attribute__((always_inline)) {
+    if (!active(t)) return;
+    const int kv0 = t * FWD_BN;
+    if ((kv0 + FWD_BN > Nkv) || (CAUSAL && kv0 + FWD_BN - 1 > q0)) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key >= Nkv || (CAUSAL && key > qi)) s[kb][r] = -INFINITY;
+        }
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, shfl_xor32(mx));
+    const float t_new = mx * c_row;
+    const bool resc = t_new > m_used + RESCALE_SLACK;
+    if (__any(resc)) {
+      const float m_new = resc ? t_new : m_used;
+      const float alpha = resc ? fast_exp2(m_used - m_new) : 1.0f;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        o_acc[db] *= alpha;
+        if constexpr (PQ >= 0) oh_acc[db] *= alpha;
+      }
+      l_part *= alpha;
+      m_used = m_new;
+    }
+    const float m_sub = (m_used == -INFINITY) ? 0.0f : m_used;
+    FqScale fs = {0.0f, 0.0f};
+    if constexpr (PQ >= 0) {   // absmax of the row group = exp2 of its largest argument
+      const float pmax = (mx == -INFINITY) ? 0.0f : fast_exp2(__builtin_fmaf(mx, c_row, -m_sub));
+      fs = fq_scale(pmax, Fp8Fmt<FQF>::FMAX);
+    }
+    const FqScale f4[4] = {fs, fs, fs, fs};
+    float psum = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int kb = kk >> 1, h = kk & 1;
+      float p8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        p8[j] = fast_exp2(__builtin_fmaf(s[kb][8 * h + j], c_row, -m_sub));
+        psum += p8[j];
+      }
+      uint32_t w8[8];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) w8[4 + jj] = DT::pack2(p8[2 * jj], p8[2 * jj + 1]);
+      if constexpr (PQ >= 0) {
+#pragma unroll
+        for (int jq = 0; jq < 2; ++jq) {
+          const f32x4 xq = fq_quad<FQF>(&p8[4 * jq], f4);
+          w8[2 * jq] = DT::pack2(xq[0], xq[1]);
+          w8[2 * jq + 1] = DT::pack2(xq[2], xq[3]);
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) w8[jj] = w8[4 + jj];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s[kb][8 * h + j] = __builtin_bit_cast(float, w8[j]);
+    }
+    l_part += psum;
+  };
+
+  // prologue: K(0) (and its scales) resident before phase 0
+  if (T > 0 && grp == 0) {
+    copy.issue(kbuf[0], kp, 0, Nkv);
+    if constexpr (QKS) {
+      if (tid < FWD_BN) ksreg = tid < Nkv ? ksp[tid] : 0.0f;
+    }
+  }
+  wait_vmem();
+  if constexpr (QKS) {
+    if (T > 0 && tid < FWD_BN) ks_s[0][tid] = ksreg;
+  }
+  __syncthreads();
+  // Tile copies are issued only by group 0, in its VALU phases (2t+1: K(t+1)
+  // and V(t), into the buffers last read in phase 2t-1), and waited for
+  // before that phase's barrier: no wave ever reads LDS while a copy of its
+  // own is in flight, so the MFMA phases carry no wait on global memory.
+  const int nphase = 2 * T + 2;
+  for (int ph_i = 0; ph_i < nphase; ++ph_i) {
+    // group 0: MFMA on even phases, VALU on odd; group 1 one phase later
+    const bool mfma_now = ((ph_i + grp) & 1) == 0;
+    const int t_work = (ph_i - grp) >> 1;
+    // The VALU part comes first in program order and ends with the wait for
+    // this wave's copies, so the LDS reads of the MFMA part (executed under
+    // the complementary lane mask) never wait on global memory.
+    if (!mfma_now) {
+      const int t = ph_i >> 1;
+      if (grp == 0) {
+        if (t + 1 < T) {
+          copy.issue(kbuf[(t + 1) & 1], kp, (t + 1) * FWD_BN, Nkv);
+          if constexpr (QKS) {
+            const int key = (t + 1) * FWD_BN + tid;
+            if (tid < FWD_BN) ksreg = key < Nkv ? ksp[key] : 0.0f;
+          }
+        }
+        if (t < T) copy.issue(vbuf[t & 1], vp, t * FWD_BN, Nkv);
+      }
+      if (t_work >= 0 && t_work < T) valu_phase(t_work);
+    }
+    wait_vmem();
+    if constexpr (QKS) {
+      const int t = ph_i >> 1;
+      if (grp == 0 && !mfma_now && t + 1 < T && tid < FWD_BN) ks_s[(t + 1) & 1][tid] = ksreg;
+    }
+    if (mfma_now) {   // raised issue priority: the MFMAs go first, the other wave's VALU work fills in
+      prio_mfma();
+      mfma_phase(t_work);
+      prio_valu();
+    }
+    if (ph_i + 1 < nphase) __syncthreads();
+  }
+
+  // ---- epilogue
+  if (qi >= Nq) return;
+  const float l = l_part + shfl_xor32(l_part);
+  const float inv_l = 1.0f / l;
+  uint16_t* op = (uint16_t*)a.o + (size_t)bh * Nq * D;
+  uint16_t* ohp = (uint16_t*)a.o_hp + (size_t)bh * Nq * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int d = db * 32 + 8 * u + 4 * g;
+      float x[4], y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = o_acc[db][4 * u + e] * inv_l;
+        y[e] = (PQ >= 0 ? oh_acc[db][4 * u + e] : o_acc[db][4 * u + e]) * inv_l;
+      }
+      *reinterpret_cast<u32x2*>(op + (size_t)qi * D + d) = (u32x2){DT::pack2(x[0], x[1]), DT::pack2(x[2], x[3])};
+      *reinterpret_cast<u32x2*>(ohp + (size_t)qi * D + d) = (u32x2){DT::pack2(y[0], y[1]), DT::pack2(y[2], y[3])};
+    }
+  if (g == 0) a.lse[(size_t)bh * Nq + qi] = (m_used + __builtin_log2f(l)) * LN2;
+}
+
 template <class DT, int D, bool CAUSAL, int PQ, int IN>
 static hipError_t fwd_launch(const Shape& s, const FwdArgs& a, hipStream_t st) {
-  dim3 grid(((s.Nq + FWD_BM - 1) / FWD_BM) * s.B * s.H);
-  hipLaunchKernelGGL((fwd_kernel<DT, D, CAUSAL, PQ, IN>), grid, dim3(256), 0, st, a);
+  if constexpr (IN == IN_VFP8) {
+    dim3 grid(((s.Nq + FWD_BM - 1) / FWD_BM) * s.B * s.H);
+    hipLaunchKernelGGL((fwd_kernel<DT, D, CAUSAL, PQ, IN>), grid, dim3(256), 0, st, a);
+  } else {
+    dim3 grid(((s.Nq + PP_BM - 1) / PP_BM) * s.B * s.H);
+    hipLaunchKernelGGL((fwd_pp_kernel<DT, D, CAUSAL, PQ, IN>), grid, dim3(512), 0, st, a);
+  }
   return hipGetLastError();
 }
 

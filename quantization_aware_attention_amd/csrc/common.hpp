@@ -267,6 +267,12 @@ __device__ __forceinline__ float shfl_xor32(float x) {
 // kernels can produce (checked exhaustively by qat_selftest_exp2_monotone).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Issue priority of this wave relative to the other wave on its SIMD: raised
+// around runs of MFMAs so that they issue as soon as their operands are
+// ready, while the other wave's VALU work fills the gaps.
+__device__ __forceinline__ void prio_mfma() { __builtin_amdgcn_s_setprio(1); }
+__device__ __forceinline__ void prio_valu() { __builtin_amdgcn_s_setprio(0); }
+
 // Wave index as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
