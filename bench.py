@@ -52,7 +52,7 @@ KERNEL_TAGS = {
     "fwd_kernel": ("fwd_pp_kernel", "fwd_kernel"),
     "delta_kernel": ("delta_kernel",),
     "dq_kernel": ("dq_kernel",),
-    "dkdv_kernel": ("dkdv_kernel",),
+    "dkdv_kernel": ("dkdv_sp_kernel",),
     "token_quant_kernel": ("token_quant_kernel",),
 }
 

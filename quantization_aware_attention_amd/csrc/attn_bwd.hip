@@ -97,36 +97,6 @@ struct BwdArgs {
   float c;              // sm_scale * log2(e)
 };
 
-// Stage one [64 x D] tile of a key/value tensor into LDS (swizzled).  For fp8
-// V the codes are dequantized with the per-channel scale and rounded to bf16.
-template <class DT, int D, bool FP8V>
-__device__ __forceinline__ void stage_kv_tile(char* dst, const uint8_t* src, const float* vscale, int key0,
-                                              int Nkv, int tid) {
-  constexpr int CH = D / 8;
-  constexpr int LPT = 64 * CH / 256;
-#pragma unroll
-  for (int u = 0; u < LPT; ++u) {
-    const int idx = tid + 256 * u, row = idx / CH, ch = idx % CH;
-    const int key = key0 + row;
-    u32x4 val = {0, 0, 0, 0};
-    if (key < Nkv) {
-      if constexpr (FP8V) {
-        const u32x2 codes = *reinterpret_cast<const u32x2*>(src + (size_t)key * D + ch * 8);
-        const f32x4 s0 = *reinterpret_cast<const f32x4*>(vscale + ch * 8);
-        const f32x4 s1 = *reinterpret_cast<const f32x4*>(vscale + ch * 8 + 4);
-        const float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const f32x2 f = __builtin_amdgcn_cvt_pk_f32_bf8((int)(codes[h >> 1] >> (16 * (h & 1))), false);
-          val[h] = BF16::pack2(f[0] * sc[2 * h], f[1] * sc[2 * h + 1]);
-        }
-      } else {
-        val = *reinterpret_cast<const u32x4*>(src + ((size_t)key * D + ch * 8) * 2);
-      }
-    }
-    *reinterpret_cast<u32x4*>(dst + tile_off<D>(row, ch)) = val;
-  }
-}
 
 // ------------------------------------------------------------------ dQ
 constexpr int DQ_BM = 128;
@@ -316,49 +286,67 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
     }
 }
 
-// ------------------------------------------------------------------ dK / dV
-// Eight waves share one block of 128 keys (two P groups) and the staged Q /
-// dO tiles: waves 0-3 ("dV waves") form S, P and the fake-quantized P^ for
-// their 32 keys and accumulate dV^T = dO^T P^; waves 4-7 ("dK waves") form S,
-// P, dP = dO V^T and dS and accumulate dK^T = Q^T dS.  S is formed by both
-// halves (identically), which costs one extra QK^T per block but leaves every
-// wave a single 64-register accumulator, so two waves fit on each SIMD.
-constexpr int DKV_BN = 128;   // keys per workgroup
-constexpr int DKV_BQ = 64;    // queries per staged tile
+// ---------------------------------------------------------------------------
+// Software-pipelined dK/dV: one wave per SIMD.
+//
+// Four waves own 128 keys (32 each) and produce dK and dV for them, walking
+// the query range in blocks of 32.  Each wave holds the whole 512-entry
+// register file: the dK/dV accumulators, the K and V operands of its keys,
+// two S/dP buffers and two sets of packed P^/dS operands.  Iteration b
+// issues as one instruction stream
+//   the matrix work  dV^T += dO^T P^(b-1), dK^T += Q^T dS(b-1),
+//                    S(b+1) = Q K^T, dP(b+1) = dO V^T, and
+//   the vector work of block b: P = exp2(S c - M), P^ = FQ(P) with the
+//                    (query, 64-key group) scales, dS = P o (dP - Delta),
+//                    packed as the next iteration's operands,
+// in eight fenced groups of MFMAs plus a slice of the vector work, so the
+// matrix core runs under the vector work of the same wave.  Q/dO blocks are
+// staged through registers: loaded from HBM in iteration b-3, written to LDS
+// slot b%4 in iteration b-2, read in iterations b-1 .. b+1.
+constexpr int DSP_BN = 128;    // keys per workgroup
+constexpr int DSP_BQ = 32;     // queries per block
+constexpr int DSP_SLOTS = 4;   // LDS block slots
 
 template <class DT, int D, bool CAUSAL, int PQ, int IN>
-__global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
   constexpr bool VFP8 = IN == IN_VFP8;
   constexpr bool QKS = IN == IN_QKS;
-  constexpr int TILE = DKV_BQ * D * 2;
+  constexpr int TILE = DSP_BQ * D * 2;
   constexpr int NDB = D / 32;
   constexpr int NKS = D / 16;
-  __shared__ __attribute__((aligned(16))) char qt_s[2][TILE];
-  __shared__ __attribute__((aligned(16))) char dot_s[2][TILE];
-  __shared__ __attribute__((aligned(16))) float m_s[2][DKV_BQ];
-  __shared__ __attribute__((aligned(16))) float d_s[2][DKV_BQ];
-  __shared__ __attribute__((aligned(16))) float sq_s[2][DKV_BQ];      // IN_QKS: query scales
-  __shared__ __attribute__((aligned(16))) float qs_s[2][2][DKV_BQ];   // P-quant s per (group, query)
-  __shared__ __attribute__((aligned(16))) float qr_s[2][2][DKV_BQ];   // P-quant r
+  constexpr int FQF = PQ >= 0 ? PQ : 0;
+  constexpr int NGW = DSP_BN / 64;          // 64-key P groups of the workgroup
+  constexpr int CPR = D / 8;                // 16-byte chunks per row
+  constexpr int NCH = DSP_BQ * CPR / 256;   // staged chunks per thread per tile
+  constexpr int NST2 = 4 * NDB;             // dV/dK MFMAs of a block
+  constexpr int NST = NST2 + 2 * NKS;       // + S/dP MFMAs
+  constexpr int NGRP = 8;                   // fenced groups per iteration
+  constexpr int GSZ = NST / NGRP;           // MFMAs per group
+  constexpr int AHEAD = 4;                  // MFMA steps whose LDS operand is in flight
+  static_assert(NST % NGRP == 0 && NCH >= 1, "shape");
+  __shared__ __attribute__((aligned(16))) char q_s[DSP_SLOTS][TILE];
+  __shared__ __attribute__((aligned(16))) char do_s[DSP_SLOTS][TILE];
+  __shared__ __attribute__((aligned(16))) float m_s[DSP_SLOTS][DSP_BQ];
+  __shared__ __attribute__((aligned(16))) float d_s[DSP_SLOTS][DSP_BQ];
+  __shared__ __attribute__((aligned(16))) float sq_s[DSP_SLOTS][DSP_BQ];
+  __shared__ __attribute__((aligned(16))) float qs_s[DSP_SLOTS][NGW][DSP_BQ];
+  __shared__ __attribute__((aligned(16))) float qr_s[DSP_SLOTS][NGW][DSP_BQ];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
-  const bool dk_wave = w >= 4;
-  const int kw = w & 3;
-  const int nkb = (a.Nkv + DKV_BN - 1) / DKV_BN;
+  const int nkb = (a.Nkv + DSP_BN - 1) / DSP_BN;
   const int unit = xcd_unit(blockIdx.x, gridDim.x);
   const int bh = unit / nkb;
-  const int k0 = (unit % nkb) * DKV_BN;   // causal: key block 0 sees every query: longest first
-  const int k0w = k0 + kw * 32;
+  const int k0 = (unit % nkb) * DSP_BN;   // causal: key block 0 sees every query: longest first
+  const int k0w = k0 + w * 32;
   const int kj = k0w + l32;
   const int Nq = a.Nq, Nkv = a.Nkv;
+  const int lgrp = w >> 1;                // this wave's 64-key group within the workgroup
   const int grp0 = k0 / 64;
-  const int mygrp = kw >> 1;
   const uint16_t* qp = (const uint16_t*)a.q + (size_t)bh * Nq * D;
   const uint16_t* dop = (const uint16_t*)a.dout + (size_t)bh * Nq * D;
   const uint16_t* kp = (const uint16_t*)a.k + (size_t)bh * Nkv * D;
 
-  // K^T (every wave) and V^T (dK waves) operands of this wave's 32 keys:
-  // lane holds key kj, d = 16ks + 8g .. +7
+  // K^T and V^T operands of this wave's 32 keys: lane holds key kj, d = 16ks + 8g .. +7
   s16x8 kf[NKS], vf[NKS];
   {
     const bool ok = kj < Nkv;
@@ -366,7 +354,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdArgs a) {
     for (int ks = 0; ks < NKS; ++ks) {
       kf[ks] = ok ? *reinterpret_cast<const s16x8*>(kp + (size_t)kj * D + 16 * ks + 8 * g) : (s16x8){};
       vf[ks] = (s16x8){};
-      if (dk_wave && ok) {
+      if (ok) {
         if constexpr (VFP8) {
           const uint8_t* vp = (const uint8_t*)a.v + (size_t)bh * Nkv * D;
           const float* vsc = a.v_scale + (size_t)bh * D + 16 * ks + 8 * g;
@@ -385,171 +373,286 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdArgs a) {
       }
     }
   }
-  const float sk_lane = QKS ? (kj < Nkv ? a.k_scale[(size_t)bh * Nkv + kj] : 0.0f) : 1.0f;
+  // per-key scale in the exponent; raised to the smallest normal (and 1 for
+  // absent keys) so that a masked score stays -inf after the product
+  const float sk_lane = QKS ? (kj < Nkv ? fmaxf(a.k_scale[(size_t)bh * Nkv + kj], 1.17549435e-38f) : 1.0f) : 1.0f;
+  // these loads complete here, so that no wait for them lands inside the loop
+  // (where it would also drain the block loads in flight)
+  wait_vmem();
 
-  f32x16 acc[NDB];   // dV^T (dV waves) or dK^T (dK waves)
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) acc[db] = (f32x16){};
-
-  // Q and dO tiles go HBM -> LDS directly (double-buffered); the per-query
-  // vectors (log2-domain LSE, Delta, Q scales, P-quant scales of this
-  // workgroup's two key groups) are staged through registers.
-  float vec0 = 0.0f, vec1 = 0.0f, vec2 = 0.0f;
-  auto issue_tile = [&](int t, int buf) {
-    const int qt0 = t * DKV_BQ;
-    TileCopy<D, DKV_BQ, 8> copy;   // offsets recomputed per tile: registers are tight here
-    copy.init(wave_id(), lane);
-    copy.issue(qt_s[buf], qp, qt0, Nq);
-    copy.issue(dot_s[buf], dop, qt0, Nq);
-    if (tid < DKV_BQ) {
-      const int q = qt0 + tid;
-      vec0 = q < Nq ? a.lse[(size_t)bh * Nq + q] * LOG2E : 0.0f;
-      vec1 = q < Nq ? a.delta[(size_t)bh * Nq + q] : 0.0f;
-      if constexpr (QKS) vec2 = q < Nq ? a.q_scale[(size_t)bh * Nq + q] : 1.0f;
-    } else if constexpr (PQ >= 0) {
-      if (tid < 3 * DKV_BQ) {
-        const int e = tid - DKV_BQ, gi = e / DKV_BQ, qq = e % DKV_BQ;
-        const int q = qt0 + qq, grp = grp0 + gi;
-        vec0 = (q < Nq && grp < a.NG) ? a.p_amax_in[((size_t)bh * a.NG + grp) * Nq + q] : 0.0f;
-      }
-    }
-  };
-  auto finish_tile = [&](int buf) {
-    if (tid < DKV_BQ) {
-      m_s[buf][tid] = vec0;
-      d_s[buf][tid] = vec1;
-      if constexpr (QKS) sq_s[buf][tid] = vec2;
-    } else if constexpr (PQ >= 0) {
-      if (tid < 3 * DKV_BQ) {
-        const int e = tid - DKV_BQ, gi = e / DKV_BQ, qq = e % DKV_BQ;
-        const FqScale fs = fq_scale(vec0, Fp8Fmt<(PQ >= 0 ? PQ : 0)>::FMAX);
-        qs_s[buf][gi][qq] = fs.s;
-        qr_s[buf][gi][qq] = fs.r;
-      }
-    }
-  };
-
-  const int qt_begin = CAUSAL ? (k0 / DKV_BQ) : 0;
-  const int ntq = (Nq + DKV_BQ - 1) / DKV_BQ;
+  const int qb_begin = CAUSAL ? k0 / DSP_BQ : 0;
+  const int nqb = (Nq + DSP_BQ - 1) / DSP_BQ;
+  const int NB = nqb > qb_begin ? nqb - qb_begin : 0;   // query blocks of this workgroup
   const bool wave_live = k0w < Nkv;
-  if (qt_begin < ntq) {
-    issue_tile(qt_begin, qt_begin & 1);
-    wait_vmem();
-    finish_tile(qt_begin & 1);
+  auto qstart = [&](int b) { return (qb_begin + b) * DSP_BQ; };
+  // some (query, key) pair of block b and this wave's keys is unmasked
+  auto active = [&](int b) { return wave_live && (!CAUSAL || qstart(b) + DSP_BQ - 1 >= k0w); };
+
+  // ---- staging of a block: thread tid holds chunks tid + 256i of the Q and
+  // dO tiles and vector entry tid (kind tid/32: 0 LSE, 1 Delta, 2 query
+  // scale, 3.. P-quant absmax of local group kind-3; query tid%32)
+  u32x4 stq[NCH], sto[NCH];
+  float stv = 0.0f;
+  const int e_kind = tid >> 5, e_q = tid & 31;
+  // source row of this thread's vector entry (loop-invariant); entries that
+  // are not used read LSE and are discarded, so the load is unconditional
+  // and nothing waits on it before the block is written to LDS
+  const int e_grp = grp0 + e_kind - 3;
+  const bool e_used = e_kind < 2 || (e_kind == 2 && QKS) || (PQ >= 0 && e_kind >= 3 && e_kind < 3 + NGW && e_grp < a.NG);
+  const float* e_src = a.lse + (size_t)bh * Nq;
+  if (e_used && e_kind == 1) e_src = a.delta + (size_t)bh * Nq;
+  if (e_used && e_kind == 2) e_src = a.q_scale + (size_t)bh * Nq;
+  if (e_used && e_kind >= 3) e_src = a.p_amax_in + ((size_t)bh * a.NG + e_grp) * Nq;
+  auto load_stage = [&](int b) __attribute__((always_inline)) {
+    const int q0 = qstart(b);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + 256 * i, row = c / CPR, ch = c % CPR;
+      const size_t rr = (size_t)min(q0 + row, Nq - 1);
+      stq[i] = *reinterpret_cast<const u32x4*>(qp + rr * D + 8 * ch);
+      sto[i] = *reinterpret_cast<const u32x4*>(dop + rr * D + 8 * ch);
+    }
+    stv = e_src[min(q0 + e_q, Nq - 1)];
+  };
+  auto write_tiles = [&](int b) __attribute__((always_inline)) {
+    const int slot = b & (DSP_SLOTS - 1);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + 256 * i, row = c / CPR, ch = c % CPR;
+      *reinterpret_cast<u32x4*>(q_s[slot] + tile_off<D>(row, ch)) = stq[i];
+      *reinterpret_cast<u32x4*>(do_s[slot] + tile_off<D>(row, ch)) = sto[i];
+    }
+  };
+  auto write_vec = [&](int b) __attribute__((always_inline)) {
+    const int slot = b & (DSP_SLOTS - 1);
+    const bool ok = e_used && qstart(b) + e_q < Nq;
+    if (e_kind == 0) m_s[slot][e_q] = ok ? stv * LOG2E : 0.0f;
+    else if (e_kind == 1) d_s[slot][e_q] = ok ? stv : 0.0f;
+    else if (e_kind == 2) sq_s[slot][e_q] = ok ? stv : 1.0f;
+    else if (PQ >= 0 && e_kind < 3 + NGW) {
+      const FqScale fs = fq_scale(ok ? stv : 0.0f, Fp8Fmt<FQF>::FMAX);
+      qs_s[slot][e_kind - 3][e_q] = fs.s;
+      qr_s[slot][e_kind - 3][e_q] = fs.r;
+    }
+  };
+
+  f32x16 acc_dv[NDB], acc_dk[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    acc_dv[db] = (f32x16){};
+    acc_dk[db] = (f32x16){};
   }
-  __syncthreads();
-  for (int t = qt_begin; t < ntq; ++t) {
-    const int qt0 = t * DKV_BQ;
-    const int buf = t & 1;
-    if (t + 1 < ntq) issue_tile(t + 1, buf ^ 1);
-    if (wave_live) {
-      const char* Qt = qt_s[buf];
-      const char* dOt = dot_s[buf];
+  // S/dP of a block (lane: key kj, registers: queries 8(r/4) + 4g + r%4) and
+  // its packed P^ / dS operands (query half h = words 4h .. 4h+3)
+  f32x16 sA, dpA, sB, dpB;
+  uint32_t pA[8], dsA[8], pB[8], dsB[8];
+
+  // MFMA step st of iteration b: first the k-steps of S and dP of block b+1,
+  // interleaved (Q or dO row fragment against K or V), so that they are
+  // complete when the next iteration reads them; then st >= NST1: half h,
+  // column block db, {dV, dK} of block b-1 (transposed dO or Q fragment).
+  constexpr int NST1 = NST - NST2;
+  auto fetch = [&](int b, int st_) __attribute__((always_inline)) {
+    const int st = st_ < NST1 ? st_ + NST2 : st_ - NST1;
+    if (st < NST2) {
+      const int h = st / (2 * NDB), r = st % (2 * NDB), db = r >> 1, which = r & 1;
+      const int slot = (b - 1) & (DSP_SLOTS - 1);
+      return lds_tr8<D>(which ? q_s[slot] : do_s[slot], 16 * h, 32 * db, lane);
+    }
+    const int k = st - NST2, ks = k >> 1, which = k & 1;
+    const int slot = (b + 1) & (DSP_SLOTS - 1);
+    return lds_row8<D>(which ? do_s[slot] : q_s[slot], l32, 2 * ks + g);
+  };
+  auto step = [&](const s16x8& frag, int st_, const uint32_t (&Pp)[8], const uint32_t (&DSp)[8], f32x16& S2,
+                  f32x16& DP2) __attribute__((always_inline)) {
+    const int st = st_ < NST1 ? st_ + NST2 : st_ - NST1;
+    if (st < NST2) {
+      const int h = st / (2 * NDB), r = st % (2 * NDB), db = r >> 1, which = r & 1;
+      if (which == 0) {
+        const s16x8 op = __builtin_bit_cast(s16x8, (u32x4){Pp[4 * h], Pp[4 * h + 1], Pp[4 * h + 2], Pp[4 * h + 3]});
+        acc_dv[db] = DT::mfma(frag, op, acc_dv[db]);
+      } else {
+        const s16x8 op = __builtin_bit_cast(s16x8, (u32x4){DSp[4 * h], DSp[4 * h + 1], DSp[4 * h + 2], DSp[4 * h + 3]});
+        acc_dk[db] = DT::mfma(frag, op, acc_dk[db]);
+      }
+    } else {
+      const int k = st - NST2, ks = k >> 1, which = k & 1;
+      if (k == 0) {
+        S2 = (f32x16){};
+        DP2 = (f32x16){};
+      }
+      if (which == 0) S2 = DT::mfma(frag, kf[ks], S2);
+      else DP2 = DT::mfma(frag, vf[ks], DP2);
+    }
+  };
+  // vector work of block b, per quarter u (registers 4u .. 4u+3): read the
+  // per-query vectors, form P, then quantize, form dS and pack both operands.
+  // The reads of a quarter are issued a group or more before their use.
+  float p[16];
+  f32x4 mvv[4], dvv[4], sqv[4], svv[4], rvv[4];
+  auto readvec = [&](int u, int b) __attribute__((always_inline)) {
+    const int slot = b & (DSP_SLOTS - 1), ql = 8 * u + 4 * g;
+    mvv[u] = *reinterpret_cast<const f32x4*>(&m_s[slot][ql]);
+    dvv[u] = *reinterpret_cast<const f32x4*>(&d_s[slot][ql]);
+    sqv[u] = (f32x4){1.0f, 1.0f, 1.0f, 1.0f};
+    if constexpr (QKS) sqv[u] = *reinterpret_cast<const f32x4*>(&sq_s[slot][ql]);
+    if constexpr (PQ >= 0) {
+      svv[u] = *reinterpret_cast<const f32x4*>(&qs_s[slot][lgrp][ql]);
+      rvv[u] = *reinterpret_cast<const f32x4*>(&qr_s[slot][lgrp][ql]);
+    }
+  };
+  auto form_p = [&](int u, const f32x16& S) __attribute__((always_inline)) {
 #pragma unroll
-      for (int qb2 = 0; qb2 < DKV_BQ / 32; ++qb2) {
-        const int qs = qt0 + qb2 * 32;          // first query of this 32-block
-        if (qs >= Nq) break;
-        if (CAUSAL && qs + 31 < k0w) continue;  // every key of the wave is after every query
-        // ---- S = Q K^T (lane: key kj, registers: 16 queries)
-        f32x16 sacc = (f32x16){};
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * u + e;
+      const float sr = QKS ? S[r] * sk_lane : S[r];
+      const float cr = QKS ? a.c * fmaxf(sqv[u][e], 1.17549435e-38f) : a.c;
+      p[r] = fast_exp2(__builtin_fmaf(sr, cr, -mvv[u][e]));
+    }
+  };
+  auto finish = [&](int u, const f32x16& DP, uint32_t (&Pn)[8], uint32_t (&DSn)[8]) __attribute__((always_inline)) {
+    uint32_t w0, w1;
+    if constexpr (PQ >= 0) {   // P^ = FQ(P) per (query, 64-key group)
+      const FqScale f4[4] = {{svv[u][0], rvv[u][0]}, {svv[u][1], rvv[u][1]}, {svv[u][2], rvv[u][2]},
+                             {svv[u][3], rvv[u][3]}};
+      const f32x4 xq = fq_quad<FQF>(&p[4 * u], f4);
+      w0 = DT::pack2(xq[0], xq[1]);
+      w1 = DT::pack2(xq[2], xq[3]);
+    } else {
+      w0 = DT::pack2(p[4 * u], p[4 * u + 1]);
+      w1 = DT::pack2(p[4 * u + 2], p[4 * u + 3]);
+    }
+    float dsv[4];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) sacc = DT::mfma(lds_row8<D>(Qt, qb2 * 32 + l32, 2 * ks + g), kf[ks], sacc);
-        const bool need_mask = (qs + 32 > Nq) || (k0w + 32 > Nkv) || (CAUSAL && qs < k0w + 31);
-        // ---- P = exp2(S c - M), formed exactly as in the dQ kernel
-        float p[16];
+    for (int e = 0; e < 4; ++e) {
+      dsv[e] = p[4 * u + e] * (DP[4 * u + e] - dvv[u][e]);
+      if constexpr (QKS) dsv[e] *= sqv[u][e];   // dK = sm_scale sum_i dS_ij s_q[i] code_q[i]
+    }
+    Pn[2 * u] = w0;
+    Pn[2 * u + 1] = w1;
+    DSn[2 * u] = DT::pack2(dsv[0], dsv[1]);
+    DSn[2 * u + 1] = DT::pack2(dsv[2], dsv[3]);
+  };
+  // slice j of the vector work, placed in fenced group j (NGRP == 8):
+  //   0: read 0 | 1: P 0, read 1 | 2: finish 0, read 2 | 3: P 1
+  //   4: finish 1, read 3 | 5: P 2 | 6: finish 2, P 3 | 7: finish 3
+  auto valu_piece = [&](int j, int b, const f32x16& S, const f32x16& DP, uint32_t (&Pn)[8],
+                        uint32_t (&DSn)[8]) __attribute__((always_inline)) {
+    switch (j) {
+      case 0: readvec(0, b); break;
+      case 1: form_p(0, S); readvec(1, b); break;
+      case 2: finish(0, DP, Pn, DSn); readvec(2, b); break;
+      case 3: form_p(1, S); break;
+      case 4: finish(1, DP, Pn, DSn); readvec(3, b); break;
+      case 5: form_p(2, S); break;
+      case 6: finish(2, DP, Pn, DSn); form_p(3, S); break;
+      default: finish(3, DP, Pn, DSn); break;
+    }
+  };
+
+  // iteration b: S, DP = block b (in), S2, DP2 = block b+1 (out);
+  // Pp, DSp = operands of block b-1 (in), Pn, DSn = operands of block b (out)
+  auto iteration = [&](int b, f32x16& S, f32x16& DP, f32x16& S2, f32x16& DP2, const uint32_t (&Pp)[8],
+                       const uint32_t (&DSp)[8], uint32_t (&Pn)[8], uint32_t (&DSn)[8]) __attribute__((always_inline)) {
+    const bool do2 = b >= 1 && active(b - 1);
+    const bool do1 = b + 1 < NB && active(b + 1);
+    const bool dov = b < NB && active(b);
+    const bool full = do2 && do1 && dov;
+    // staging of block b+2 (loaded in iteration b-1) and loads of block b+3:
+    // inside the first fenced groups on the full path, up front otherwise
+    const bool stw = b + 2 < NB, stl = b + 3 < NB;
+    if (!full) {
+      if (stw) {
+        write_tiles(b + 2);
+        write_vec(b + 2);
+      }
+      if (stl) load_stage(b + 3);
+    }
+    if (dov) {   // masked scores -> -inf before the exponent
+      const int q0 = qstart(b);
+      if ((q0 + DSP_BQ > Nq) || (k0w + 32 > Nkv) || (CAUSAL && q0 < k0w + 31)) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int ql = qb2 * 32 + 8 * u + 4 * g;   // local query of registers 4u..4u+3
-          const f32x4 mv = *reinterpret_cast<const f32x4*>(&m_s[buf][ql]);
-          f32x4 sq4 = {1.0f, 1.0f, 1.0f, 1.0f};
-          if constexpr (QKS) sq4 = *reinterpret_cast<const f32x4*>(&sq_s[buf][ql]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * u + e;
-            const float sr = QKS ? sacc[r] * sk_lane : sacc[r];
-            const float cr = QKS ? a.c * sq4[e] : a.c;
-            p[r] = fast_exp2(__builtin_fmaf(sr, cr, -mv[e]));
-          }
-        }
-        if (need_mask) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int q = qs + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (q >= Nq || kj >= Nkv || (CAUSAL && kj > q)) p[r] = 0.0f;
-          }
-        }
-        if (!dk_wave) {
-          // ---- dV waves: P^ = FQ(P) per (query, 64-key group); dV^T += dO^T P^
-          uint32_t wp[8];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int ql = qb2 * 32 + 8 * u + 4 * g;
-            if constexpr (PQ >= 0) {
-              const f32x4 sv = *reinterpret_cast<const f32x4*>(&qs_s[buf][mygrp][ql]);
-              const f32x4 rv = *reinterpret_cast<const f32x4*>(&qr_s[buf][mygrp][ql]);
-              const FqScale f4[4] = {{sv[0], rv[0]}, {sv[1], rv[1]}, {sv[2], rv[2]}, {sv[3], rv[3]}};
-              const f32x4 xq = fq_quad<(PQ >= 0 ? PQ : 0)>(&p[4 * u], f4);
-              wp[2 * u] = DT::pack2(xq[0], xq[1]);
-              wp[2 * u + 1] = DT::pack2(xq[2], xq[3]);
-            } else {
-              wp[2 * u] = DT::pack2(p[4 * u], p[4 * u + 1]);
-              wp[2 * u + 1] = DT::pack2(p[4 * u + 2], p[4 * u + 3]);
-            }
-          }
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const s16x8 p_op = __builtin_bit_cast(s16x8, (u32x4){wp[4 * h], wp[4 * h + 1], wp[4 * h + 2], wp[4 * h + 3]});
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-              acc[db] = DT::mfma(lds_tr8<D>(dOt, qb2 * 32 + 16 * h, db * 32, lane), p_op, acc[db]);
-          }
-        } else {
-          // ---- dK waves: dP = dO V^T, dS = P o (dP - Delta); dK^T += Q^T dS
-          f32x16 dp = (f32x16){};
-#pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) dp = DT::mfma(lds_row8<D>(dOt, qb2 * 32 + l32, 2 * ks + g), vf[ks], dp);
-          uint32_t wd[8];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int ql = qb2 * 32 + 8 * u + 4 * g;
-            const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&d_s[buf][ql]);
-            f32x4 sq4 = {1.0f, 1.0f, 1.0f, 1.0f};
-            if constexpr (QKS) sq4 = *reinterpret_cast<const f32x4*>(&sq_s[buf][ql]);
-            float dsv[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              dsv[e] = p[4 * u + e] * (dp[4 * u + e] - dv4[e]);
-              if constexpr (QKS) dsv[e] *= sq4[e];   // dK = sm_scale sum_i dS_ij s_q[i] code_q[i]
-            }
-            wd[2 * u] = DT::pack2(dsv[0], dsv[1]);
-            wd[2 * u + 1] = DT::pack2(dsv[2], dsv[3]);
-          }
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const s16x8 ds_op = __builtin_bit_cast(s16x8, (u32x4){wd[4 * h], wd[4 * h + 1], wd[4 * h + 2], wd[4 * h + 3]});
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-              acc[db] = DT::mfma(lds_tr8<D>(Qt, qb2 * 32 + 16 * h, db * 32, lane), ds_op, acc[db]);
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int q = q0 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (q >= Nq || kj >= Nkv || (CAUSAL && kj > q)) S[r] = -INFINITY;
         }
       }
     }
-    wait_vmem();
-    if (t + 1 < ntq) finish_tile(buf ^ 1);
+    if (full) {
+      s16x8 ring[AHEAD];
+#pragma unroll
+      for (int st = 0; st < AHEAD; ++st) ring[st] = fetch(b, st);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < NGRP; ++j) {
+#pragma unroll
+        for (int i = 0; i < GSZ; ++i) {
+          const int st = j * GSZ + i;
+          const s16x8 cur = ring[st % AHEAD];
+          if (st + AHEAD < NST) ring[st % AHEAD] = fetch(b, st + AHEAD);
+          step(cur, st, Pp, DSp, S2, DP2);
+        }
+        valu_piece(j, b, S, DP, Pn, DSn);
+        if (j == 0 && stw) write_tiles(b + 2);
+        if (j == 1 && stw) write_vec(b + 2);
+        if (j == 2 && stl) load_stage(b + 3);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      if (do1) {
+#pragma unroll
+        for (int st = 0; st < NST1; ++st) step(fetch(b, st), st, Pp, DSp, S2, DP2);
+      }
+      if (do2) {
+#pragma unroll
+        for (int st = NST1; st < NST; ++st) step(fetch(b, st), st, Pp, DSp, S2, DP2);
+      }
+      if (dov) {
+#pragma unroll
+        for (int j = 0; j < NGRP; ++j) valu_piece(j, b, S, DP, Pn, DSn);
+      }
+    }
     __syncthreads();
+  };
+
+  // prologue: blocks 0 and 1 in LDS, block 2 staged, S/dP of block 0
+  if (NB > 0) {
+    load_stage(0);
+    write_tiles(0);
+    write_vec(0);
+  }
+  if (NB > 1) {
+    load_stage(1);
+    write_tiles(1);
+    write_vec(1);
+  }
+  if (NB > 2) load_stage(2);
+  __syncthreads();
+  if (NB > 0 && active(0)) {
+#pragma unroll
+    for (int st = 0; st < NST1; ++st) step(fetch(-1, st), st, pB, dsB, sA, dpA);
+  }
+  for (int b = 0; b <= NB; b += 2) {
+    iteration(b, sA, dpA, sB, dpB, pB, dsB, pA, dsA);
+    if (b + 1 <= NB) iteration(b + 1, sB, dpB, sA, dpA, pA, dsA, pB, dsB);
   }
 
   if (kj >= Nkv) return;
-  uint16_t* outp = (uint16_t*)(dk_wave ? a.dk : a.dv) + (size_t)bh * Nkv * D;
-  const float scale = dk_wave ? a.sm_scale : 1.0f;
+  uint16_t* dkp = (uint16_t*)a.dk + (size_t)bh * Nkv * D;
+  uint16_t* dvp = (uint16_t*)a.dv + (size_t)bh * Nkv * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int d = db * 32 + 8 * u + 4 * g;
-      const float x[4] = {acc[db][4 * u] * scale, acc[db][4 * u + 1] * scale, acc[db][4 * u + 2] * scale,
-                          acc[db][4 * u + 3] * scale};
-      *reinterpret_cast<u32x2*>(outp + (size_t)kj * D + d) = (u32x2){DT::pack2(x[0], x[1]), DT::pack2(x[2], x[3])};
+      float x[4], y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = acc_dk[db][4 * u + e] * a.sm_scale;
+        y[e] = acc_dv[db][4 * u + e];
+      }
+      *reinterpret_cast<u32x2*>(dkp + (size_t)kj * D + d) = (u32x2){DT::pack2(x[0], x[1]), DT::pack2(x[2], x[3])};
+      *reinterpret_cast<u32x2*>(dvp + (size_t)kj * D + d) = (u32x2){DT::pack2(y[0], y[1]), DT::pack2(y[2], y[3])};
     }
 }
 
@@ -563,7 +666,7 @@ struct DqK {
 template <class DT, int D, bool CAUSAL, int PQ, int IN>
 struct DkvK {
   static void run(dim3 g, const BwdArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((dkdv_kernel<DT, D, CAUSAL, PQ, IN>), g, dim3(512), 0, st, a);
+    hipLaunchKernelGGL((dkdv_sp_kernel<DT, D, CAUSAL, PQ, IN>), g, dim3(256), 0, st, a);
   }
 };
 
@@ -632,7 +735,7 @@ hipError_t launch_bwd_dkdv(const Shape& s, const Inputs& in, const void* dout, c
   a.p_amax_in = p_amax;
   a.dk = dk;
   a.dv = dv;
-  dim3 grid(((s.Nkv + DKV_BN - 1) / DKV_BN) * s.B * s.H);
+  dim3 grid(((s.Nkv + DSP_BN - 1) / DSP_BN) * s.B * s.H);
   return pick_all<DkvK>(s, grid, a, causal, pfmt, in.mode, st);
 }
 
