@@ -317,7 +317,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   constexpr int NKS = D / 16;
   constexpr int FQF = PQ >= 0 ? PQ : 0;
   constexpr int NPV = 4 * NDB;   // P@V steps of an MFMA phase
-  constexpr int PP_AHEAD = 2;    // steps whose LDS operands are in flight
+  constexpr int PP_AHEAD = QKS ? 2 : 6;   // fragments in flight ahead of their MFMAs (key scales need registers)
   __shared__ __attribute__((aligned(16))) char kbuf[2][TILE];
   __shared__ __attribute__((aligned(16))) char vbuf[2][TILE];
   __shared__ __attribute__((aligned(16))) float ks_s[2][FWD_BN];   // IN_QKS: key scales of K(t)
@@ -380,73 +380,68 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
         }
     }
   };
-  // The MFMA phase as one stream of steps: NPV steps of P@V (one V fragment,
-  // the O and O_hp MFMAs of a 16-key by 32-column block) then NKS steps of
-  // S^T = K Q^T (a Q fragment and two K fragments, two MFMAs).  Step st
-  // reads the fragments of step st + PP_AHEAD; scheduling fences keep that
-  // order, so every MFMA finds its LDS operands already loaded.
-  struct Bundle { s16x8 a, b, c; };
-  auto fetch = [&](const char* Vt, const char* Kt, int st) __attribute__((always_inline)) {
-    Bundle r;
-    if (st < NPV) {
-      r.a = lds_tr8<D>(Vt, (st / NDB) * 16, (st % NDB) * 32, lane);
-    } else {
-      const int ks = st - NPV;
-      r.a = lds_row8<D>(qbuf, w * 32 + l32, 2 * ks + g);
-      r.b = lds_row8<D>(Kt, l32, 2 * ks + g);
-      r.c = lds_row8<D>(Kt, 32 + l32, 2 * ks + g);
-    }
-    return r;
+  // The MFMA phase as one stream of single-fragment steps: NPV steps of
+  // P@V (a V fragment feeding the O and O_hp MFMAs of a 16-key by 32-column
+  // block), then for each k-step of S^T = K Q^T a Q fragment and the two K
+  // fragments (one MFMA each, against the last Q fragment).  Step f reads the
+  // fragment of step f + PP_AHEAD; scheduling fences keep that order, so every
+  // MFMA finds its LDS operand already loaded.
+  constexpr int NFR = NPV + 3 * NKS;
+  auto fetch = [&](const char* Vt, const char* Kt, int f) __attribute__((always_inline)) {
+    if (f < NPV) return lds_tr8<D>(Vt, (f / NDB) * 16, (f % NDB) * 32, lane);
+    const int k = f - NPV, ks = k / 3, part = k % 3;
+    if (part == 0) return lds_row8<D>(qbuf, w * 32 + l32, 2 * ks + g);
+    return lds_row8<D>(Kt, (part - 1) * 32 + l32, 2 * ks + g);
   };
-  auto step = [&](const Bundle& cur, int st) __attribute__((always_inline)) {
-    if (st < NPV) {   // O^T += V^T P^T, k-step kk, column block db
-      const int kk = st / NDB, db = st % NDB, kb = kk >> 1, o8 = 8 * (kk & 1);
+  s16x8 qcur;
+  auto step = [&](const s16x8& frag, int f) __attribute__((always_inline)) {
+    if (f < NPV) {   // O^T += V^T P^T, k-step kk, column block db
+      const int kk = f / NDB, db = f % NDB, kb = kk >> 1, o8 = 8 * (kk & 1);
       const s16x8 bhp = __builtin_bit_cast(s16x8, (f32x4){s[kb][o8 + 4], s[kb][o8 + 5], s[kb][o8 + 6], s[kb][o8 + 7]});
       if constexpr (PQ >= 0) {
         const s16x8 bq = __builtin_bit_cast(s16x8, (f32x4){s[kb][o8], s[kb][o8 + 1], s[kb][o8 + 2], s[kb][o8 + 3]});
-        o_acc[db] = DT::mfma(cur.a, bq, o_acc[db]);
-        oh_acc[db] = DT::mfma(cur.a, bhp, oh_acc[db]);
+        o_acc[db] = DT::mfma(frag, bq, o_acc[db]);
+        oh_acc[db] = DT::mfma(frag, bhp, oh_acc[db]);
       } else {
-        o_acc[db] = DT::mfma(cur.a, bhp, o_acc[db]);
+        o_acc[db] = DT::mfma(frag, bhp, o_acc[db]);
       }
     } else {          // S^T = K Q^T, k-step ks
-      if (st == NPV) {
+      const int k = f - NPV, part = k % 3;
+      if (k == 0) {
         s[0] = (f32x16){};
         s[1] = (f32x16){};
       }
-      s[0] = DT::mfma(cur.b, cur.a, s[0]);
-      s[1] = DT::mfma(cur.c, cur.a, s[1]);
+      if (part == 0) qcur = frag;
+      else s[part - 1] = DT::mfma(frag, qcur, s[part - 1]);
     }
   };
   auto mfma_phase = [&](int t) __attribute__((always_inline)) {
     const bool do_pv = t >= 1 && active(t - 1);
     const bool do_qk = t < T && active(t);
+    const char* Vt = vbuf[(t - 1) & 1];
+    const char* Kt = kbuf[t & 1];
     if (do_pv && do_qk) {
-      const char* Vt = vbuf[(t - 1) & 1];
-      const char* Kt = kbuf[t & 1];
-      Bundle ring[PP_AHEAD];
+      s16x8 ring[PP_AHEAD];
 #pragma unroll
-      for (int st = 0; st < PP_AHEAD; ++st) ring[st] = fetch(Vt, Kt, st);
+      for (int f = 0; f < PP_AHEAD; ++f) ring[f] = fetch(Vt, Kt, f);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int st = 0; st < NPV + NKS; ++st) {
-        const Bundle cur = ring[st % PP_AHEAD];
-        if (st + PP_AHEAD < NPV + NKS) ring[st % PP_AHEAD] = fetch(Vt, Kt, st + PP_AHEAD);
+      for (int f = 0; f < NFR; ++f) {
+        const s16x8 cur = ring[f % PP_AHEAD];
+        if (f + PP_AHEAD < NFR) ring[f % PP_AHEAD] = fetch(Vt, Kt, f + PP_AHEAD);
         __builtin_amdgcn_sched_barrier(0);
-        step(cur, st);
+        step(cur, f);
         __builtin_amdgcn_sched_barrier(0);
       }
       scale_keys(t);
     } else {          // first and last phases, causal edges: the same steps unpipelined
-      const char* Vt = vbuf[(t - 1) & 1];
-      const char* Kt = kbuf[t & 1];
       if (do_pv) {
 #pragma unroll
-        for (int st = 0; st < NPV; ++st) step(fetch(Vt, Kt, st), st);
+        for (int f = 0; f < NPV; ++f) step(fetch(Vt, Kt, f), f);
       }
       if (do_qk) {
 #pragma unroll
-        for (int st = NPV; st < NPV + NKS; ++st) step(fetch(Vt, Kt, st), st);
+        for (int f = NPV; f < NFR; ++f) step(fetch(Vt, Kt, f), f);
         scale_keys(t);
       }
     }
