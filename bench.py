@@ -204,6 +204,21 @@ def main():
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
 
+    # ---- median and minimum per call of the forward, the backward (from the
+    # saved forward outputs) and the whole step, one event pair per call
+    def per_call(fn, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in evs)
+        return {"median": round(ts[len(ts) // 2], 4), "min": round(ts[0], 4)}
+
+    split_ms = {"fwd": per_call(fwd, max(args.steps, 20)), "bwd": per_call(bwd, max(args.steps, 20)),
+                "step": per_call(step, max(args.steps, 20))}
+
     Wn = w.B * w.H * w.Nq * w.Nkv * w.D
     if w.causal:
         Wn = Wn * (w.Nq + 1) / (2 * w.Nq)
@@ -284,7 +299,7 @@ def main():
                                f"{', Q/K/V fake-quant e4m3' if w.qkv_quant else ''}"
                                f"{', V e5m2' if w.v_fp8 else ''}",
                    "credited_flop_per_step": credited, "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-                   "fa_convention_tflops": round(fa_conv, 2)},
+                   "fa_convention_tflops": round(fa_conv, 2), "call_ms": split_ms},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernel_source_hash": kernel_source_hash(),
