@@ -47,12 +47,13 @@ def parse():
 
 
 # stage label -> kernels that implement it (the forward has a ping-pong kernel
-# for value inputs and a separate one for fp8 V)
+# for value inputs and a separate one for fp8 V; the dK/dV stage adds a small
+# merge kernel when it splits its last key blocks over query ranges)
 KERNEL_TAGS = {
     "fwd_kernel": ("fwd_pp_kernel", "fwd_kernel"),
     "delta_kernel": ("delta_kernel",),
     "dq_kernel": ("dq_kernel",),
-    "dkdv_kernel": ("dkdv_sp_kernel",),
+    "dkdv_kernel": ("dkdv_sp_kernel", "dkdv_merge_kernel"),
     "token_quant_kernel": ("token_quant_kernel",),
 }
 
@@ -73,7 +74,9 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, copy_mib: int):
     from collections import defaultdict
 
     def load(path, counter):
-        per = defaultdict(list)
+        # bytes per stage call: the mean over dispatches of each kernel,
+        # summed over the kernels of the stage
+        per = defaultdict(lambda: defaultdict(list))
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
                 continue
@@ -82,8 +85,8 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, copy_mib: int):
             if "copyBuffer" in name:
                 tag = "copy"
             if tag:
-                per[tag].append(float(r["Counter_Value"]) * 1024.0)
-        return {t: sum(v) / len(v) for t, v in per.items()}
+                per[tag][name.split("<")[0]].append(float(r["Counter_Value"]) * 1024.0)
+        return {t: sum(sum(v) / len(v) for v in ks.values()) for t, ks in per.items()}
 
     fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
     known = float(copy_mib << 20)
@@ -225,7 +228,8 @@ def main():
     credited = 16.0 * Wn
     value = credited / (ms_step * 1e-3) / 1e12
 
-    # ---- per-kernel durations (each call below launches exactly one kernel)
+    # ---- per-stage durations (each call below launches one kernel, and the
+    # dK/dV stage at most one more: the merge of split key blocks)
     kernels = {
         "fwd_kernel": (fwd, 6.0 * Wn),
         "delta_kernel": (lambda: bwd(ops.QAT_BWD_DELTA), None),

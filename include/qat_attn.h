@@ -109,7 +109,10 @@ int qat_attn_fwd(const qat_attn_dims* dims, const void* q, const void* k, const 
  * Writes dq [B,H,Nq,D], dk, dv [B,H,Nkv,D] (dtype; dv is the gradient with
  * respect to the dequantized V^ when V is fp8) as straight-through gradients
  * of the un-quantized inputs.  Delta = rowsum(dout o o_hp) is kept in the
- * workspace (>= qat_attn_workspace_bytes(dims, flags, 1) bytes).
+ * workspace (>= qat_attn_workspace_bytes(dims, flags, 1) bytes), and so are
+ * fp32 partial sums of dk, dv when the last 128-key blocks of a launch are
+ * split over query ranges to fill the device (added in a fixed order: the
+ * result stays bitwise reproducible on a given device).
  * Errors as for qat_attn_fwd.
  */
 int qat_attn_bwd(const qat_attn_dims* dims, const void* q, const void* k, const void* v,

@@ -19,12 +19,15 @@ inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Workspace layout (each piece 256-byte aligned, in this order):
-//   bwd: delta fp32 [B,H,Nq]; p_amax fp32 [B,H,ceil(Nkv/64),Nq] (P quant only)
+//   bwd: delta fp32 [B,H,Nq]; p_amax fp32 [B,H,ceil(Nkv/64),Nq] (P quant only);
+//   fp32 partial dK/dV of key blocks split over query ranges
 //   fwd and bwd, when Q/K/V quantization is on: the fp8 code values of Q and
 //   K (dtype) with their per-token scales (fp32 [B,H,Nq], [B,H,Nkv]), and
 //   V^ = code * scale rounded to the dtype
+qat::Shape shape_of(const qat_attn_dims& d) { return qat::Shape{d.B, d.H, d.Nq, d.Nkv, d.D, d.dtype}; }
+
 struct Layout {
-  size_t delta = 0, amax = 0, qh = 0, kh = 0, vh = 0, qs = 0, ks = 0, total = 0;
+  size_t delta = 0, amax = 0, part = 0, qh = 0, kh = 0, vh = 0, qs = 0, ks = 0, total = 0;
 };
 
 Layout layout(const qat_attn_dims& d, uint32_t flags, int pass) {
@@ -39,6 +42,8 @@ Layout layout(const qat_attn_dims& d, uint32_t flags, int pass) {
       const size_t ng = ((size_t)d.Nkv + QAT_ATTN_P_GROUP - 1) / QAT_ATTN_P_GROUP;
       off += align_up(BH * ng * d.Nq * sizeof(float));
     }
+    L.part = off;
+    off += align_up(qat::dkdv_part_bytes(shape_of(d)));
   }
   if (flags & QAT_QKV_QUANT) {
     L.qh = off;
@@ -81,7 +86,6 @@ int check_common(const qat_attn_dims* dims, float sm_scale, int causal, uint32_t
 
 int check_ptr(const void* p) { return (p && aligned16(p)) ? QAT_OK : QAT_EINVAL; }
 
-qat::Shape shape_of(const qat_attn_dims& d) { return qat::Shape{d.B, d.H, d.Nq, d.Nkv, d.D, d.dtype}; }
 
 int pfmt_of(uint32_t flags) {
   if (!(flags & QAT_P_QUANT)) return -1;
@@ -181,7 +185,8 @@ int qat_attn_bwd_stages(const qat_attn_dims* dims, const void* q, const void* k,
   if (stages & QAT_BWD_DQ)
     QAT_TRY(qat::launch_bwd_dq(s, in, dout, lse, delta, sm_scale, causal != 0, pfmt, dq, amax, st));
   if (stages & QAT_BWD_DKDV)
-    QAT_TRY(qat::launch_bwd_dkdv(s, in, dout, lse, delta, amax, sm_scale, causal != 0, pfmt, dk, dv, st));
+    QAT_TRY(qat::launch_bwd_dkdv(s, in, dout, lse, delta, amax, sm_scale, causal != 0, pfmt, dk, dv,
+                                 reinterpret_cast<float*>(ws + L.part), st));
   return QAT_OK;
 }
 

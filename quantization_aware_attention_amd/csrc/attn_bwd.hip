@@ -92,6 +92,9 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
+  float* dkdv_part;     // fp32 partial dK/dV of split key blocks
+  int n_whole;          // dK/dV: key blocks run whole by one workgroup each
+  int n_split;          // dK/dV: query-range parts of each remaining key block
   int Nq, Nkv, NG;
   float sm_scale;
   float c;              // sm_scale * log2(e)
@@ -334,7 +337,18 @@ __global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int nkb = (a.Nkv + DSP_BN - 1) / DSP_BN;
-  const int unit = xcd_unit(blockIdx.x, gridDim.x);
+  // Workgroups [0, n_whole) take whole key blocks; the rest take one of
+  // n_split query ranges of the last key blocks, which would otherwise run
+  // alone in a last, mostly idle round of the chip.
+  int unit, part = 0, nparts = 1;
+  if ((int)blockIdx.x < a.n_whole) {
+    unit = xcd_unit(blockIdx.x, a.n_whole);
+  } else {
+    const int j = xcd_unit(blockIdx.x - a.n_whole, gridDim.x - a.n_whole);
+    unit = a.n_whole + j / a.n_split;
+    part = j % a.n_split;
+    nparts = a.n_split;
+  }
   const int bh = unit / nkb;
   const int k0 = (unit % nkb) * DSP_BN;   // causal: key block 0 sees every query: longest first
   const int k0w = k0 + w * 32;
@@ -380,9 +394,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
   // (where it would also drain the block loads in flight)
   wait_vmem();
 
-  const int qb_begin = CAUSAL ? k0 / DSP_BQ : 0;
+  const int qb_first = CAUSAL ? k0 / DSP_BQ : 0;
   const int nqb = (Nq + DSP_BQ - 1) / DSP_BQ;
-  const int NB = nqb > qb_begin ? nqb - qb_begin : 0;   // query blocks of this workgroup
+  const int NB_all = nqb > qb_first ? nqb - qb_first : 0;
+  const int qb_begin = qb_first + NB_all * part / nparts;
+  const int NB = qb_first + NB_all * (part + 1) / nparts - qb_begin;   // query blocks of this workgroup
   const bool wave_live = k0w < Nkv;
   auto qstart = [&](int b) { return (qb_begin + b) * DSP_BQ; };
   // some (query, key) pair of block b and this wave's keys is unmasked
@@ -638,6 +654,21 @@ __global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
   }
 
   if (kj >= Nkv) return;
+  if (nparts > 1) {   // unscaled fp32 partials [slot][dK, dV][key of the block][D]
+    float* pw = a.dkdv_part + (size_t)((unit - a.n_whole) * nparts + part) * 2 * DSP_BN * D;
+    const int kl = w * 32 + l32;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int d = db * 32 + 8 * u + 4 * g;
+        *reinterpret_cast<f32x4*>(pw + (size_t)kl * D + d) =
+            (f32x4){acc_dk[db][4 * u], acc_dk[db][4 * u + 1], acc_dk[db][4 * u + 2], acc_dk[db][4 * u + 3]};
+        *reinterpret_cast<f32x4*>(pw + (size_t)(DSP_BN + kl) * D + d) =
+            (f32x4){acc_dv[db][4 * u], acc_dv[db][4 * u + 1], acc_dv[db][4 * u + 2], acc_dv[db][4 * u + 3]};
+      }
+    return;
+  }
   uint16_t* dkp = (uint16_t*)a.dk + (size_t)bh * Nkv * D;
   uint16_t* dvp = (uint16_t*)a.dv + (size_t)bh * Nkv * D;
 #pragma unroll
@@ -654,6 +685,31 @@ __global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
       *reinterpret_cast<u32x2*>(dkp + (size_t)kj * D + d) = (u32x2){DT::pack2(x[0], x[1]), DT::pack2(x[2], x[3])};
       *reinterpret_cast<u32x2*>(dvp + (size_t)kj * D + d) = (u32x2){DT::pack2(y[0], y[1]), DT::pack2(y[2], y[3])};
     }
+}
+
+// Sum of the query-range partials of each split key block, in part order
+// (deterministic), scaled and rounded like the whole-block epilogue.  Thread
+// t of workgroup (block, z) handles four consecutive d of one key.
+template <class DT, int D>
+__global__ __launch_bounds__(256) void dkdv_merge_kernel(BwdArgs a, int nkb) {
+  constexpr int PER_BLOCK = DSP_BN * D / 4;   // threads per key block
+  const int i = blockIdx.y * 256 + threadIdx.x;
+  if (i >= PER_BLOCK) return;
+  const int kl = i / (D / 4), d = 4 * (i % (D / 4));
+  const int unit = a.n_whole + blockIdx.x;
+  const int bh = unit / nkb, key = (unit % nkb) * DSP_BN + kl;
+  if (key >= a.Nkv) return;
+  const float* pw = a.dkdv_part + (size_t)blockIdx.x * a.n_split * 2 * DSP_BN * D;
+  f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < a.n_split; ++p) {
+    const float* q = pw + (size_t)p * 2 * DSP_BN * D;
+    sk += *reinterpret_cast<const f32x4*>(q + (size_t)kl * D + d);
+    sv += *reinterpret_cast<const f32x4*>(q + (size_t)(DSP_BN + kl) * D + d);
+  }
+  const size_t o = ((size_t)bh * a.Nkv + key) * D + d;
+  *reinterpret_cast<u32x2*>((uint16_t*)a.dk + o) =
+      (u32x2){DT::pack2(sk[0] * a.sm_scale, sk[1] * a.sm_scale), DT::pack2(sk[2] * a.sm_scale, sk[3] * a.sm_scale)};
+  *reinterpret_cast<u32x2*>((uint16_t*)a.dv + o) = (u32x2){DT::pack2(sv[0], sv[1]), DT::pack2(sv[2], sv[3])};
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -728,15 +784,67 @@ hipError_t launch_bwd_dq(const Shape& s, const Inputs& in, const void* dout, con
   return pick_all<DqK>(s, grid, a, causal, pfmt, in.mode, st);
 }
 
+size_t dkdv_part_bytes(const Shape& s) {
+  const long long units = (long long)((s.Nkv + DSP_BN - 1) / DSP_BN) * s.B * s.H;
+  const long long slots = units * DKDV_MAX_SPLIT < DKDV_PART_SLOTS ? units * DKDV_MAX_SPLIT : DKDV_PART_SLOTS;
+  return (size_t)slots * 2 * DSP_BN * s.D * sizeof(float);
+}
+
+// Tail split: with U key blocks on C compute units, the last U mod C blocks
+// would run in a round of their own.  When they fill at most half of it,
+// each is cut into n_split query ranges (as many as fit in that round, at
+// most DKDV_MAX_SPLIT) whose partial sums a merge kernel adds up.  Causal
+// launches already order their blocks longest first and are left whole.
+static void plan_dkdv(const Shape& s, bool causal, int cus, BwdArgs* a) {
+  const int nkb = (s.Nkv + DSP_BN - 1) / DSP_BN;
+  const int units = nkb * s.B * s.H;
+  const int nqb = (s.Nq + DSP_BQ - 1) / DSP_BQ;
+  a->n_whole = units;
+  a->n_split = 1;
+  if (causal || cus <= 0 || !a->dkdv_part) return;
+  const int rem = units % cus;
+  if (rem == 0 || 2 * rem > cus) return;
+  int split = cus / rem;
+  if (split > DKDV_MAX_SPLIT) split = DKDV_MAX_SPLIT;
+  if (split > nqb) split = nqb;
+  if (split < 2 || (long long)rem * split > DKDV_PART_SLOTS) return;
+  a->n_whole = units - rem;
+  a->n_split = split;
+}
+
+template <class DT, int D>
+static void launch_merge(const BwdArgs& a, int nkb, int nblocks, hipStream_t st) {
+  dim3 grid((unsigned)nblocks, (unsigned)((DSP_BN * D / 4 + 255) / 256));
+  hipLaunchKernelGGL((dkdv_merge_kernel<DT, D>), grid, dim3(256), 0, st, a, nkb);
+}
+
 hipError_t launch_bwd_dkdv(const Shape& s, const Inputs& in, const void* dout, const float* lse,
                            const float* delta, const float* p_amax, float sm_scale, bool causal,
-                           int pfmt, void* dk, void* dv, hipStream_t st) {
+                           int pfmt, void* dk, void* dv, float* part_ws, hipStream_t st) {
   BwdArgs a = make_args(s, in, dout, lse, delta, sm_scale);
   a.p_amax_in = p_amax;
   a.dk = dk;
   a.dv = dv;
-  dim3 grid(((s.Nkv + DSP_BN - 1) / DSP_BN) * s.B * s.H);
-  return pick_all<DkvK>(s, grid, a, causal, pfmt, in.mode, st);
+  a.dkdv_part = part_ws;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 0;
+  plan_dkdv(s, causal, cus, &a);
+  const int nkb = (s.Nkv + DSP_BN - 1) / DSP_BN;
+  const int units = nkb * s.B * s.H;
+  const int split_blocks = units - a.n_whole;
+  dim3 grid((unsigned)(a.n_whole + split_blocks * a.n_split));
+  hipError_t e = pick_all<DkvK>(s, grid, a, causal, pfmt, in.mode, st);
+  if (e != hipSuccess || split_blocks == 0) return e;
+  if (s.dtype == 0) {
+    if (s.D == 128) launch_merge<BF16, 128>(a, nkb, split_blocks, st);
+    else launch_merge<BF16, 64>(a, nkb, split_blocks, st);
+  } else {
+    if (s.D == 128) launch_merge<FP16, 128>(a, nkb, split_blocks, st);
+    else launch_merge<FP16, 64>(a, nkb, split_blocks, st);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace qat

@@ -54,8 +54,16 @@ hipError_t launch_bwd_delta(const Shape& s, const void* o_hp, const void* dout, 
 hipError_t launch_bwd_dq(const Shape& s, const Inputs& in, const void* dout, const float* lse,
                          const float* delta, float sm_scale, bool causal, int pfmt,
                          void* dq, float* p_amax, hipStream_t st);
+// part_ws: fp32 scratch of dkdv_part_bytes(s) for the partial sums of key
+// blocks split over query ranges (null: no block is split).
 hipError_t launch_bwd_dkdv(const Shape& s, const Inputs& in, const void* dout, const float* lse,
                            const float* delta, const float* p_amax, float sm_scale, bool causal,
-                           int pfmt, void* dk, void* dv, hipStream_t st);
+                           int pfmt, void* dk, void* dv, float* part_ws, hipStream_t st);
+
+// dK/dV tail split: at most DKDV_MAX_SPLIT query ranges per key block and
+// DKDV_PART_SLOTS partial blocks in all.
+constexpr int DKDV_MAX_SPLIT = 4;
+constexpr int DKDV_PART_SLOTS = 256;
+size_t dkdv_part_bytes(const Shape& s);
 
 }  // namespace qat

@@ -35,6 +35,9 @@ SMALL = {
     "one_query": BASE.with_(B=1, H=2, Nq=1, Nkv=200, seed=20),
     "causal_one": BASE.with_(B=1, H=1, Nq=1, Nkv=1, causal=True, seed=21),
     "tile_aligned": BASE.with_(B=1, H=1, Nq=256, Nkv=128, seed=22),
+    # 300 key blocks of 128: on 256 compute units, 256 run whole and the last
+    # 44 are split over four query ranges whose partials are merged
+    "many_heads_tail_split": BASE.with_(B=1, H=300, Nq=128, Nkv=128, seed=24),
 }
 
 
