@@ -50,7 +50,7 @@ def parse():
 # for value inputs and a separate one for fp8 V; the dK/dV stage adds a small
 # merge kernel when it splits its last key blocks over query ranges)
 KERNEL_TAGS = {
-    "fwd_kernel": ("fwd_pp_kernel", "fwd_kernel"),
+    "fwd_kernel": ("fwd_pp_kernel", "fwd_f8v_kernel"),
     "delta_kernel": ("delta_kernel",),
     "dq_kernel": ("dq_kernel",),
     "dkdv_kernel": ("dkdv_sp_kernel", "dkdv_merge_kernel"),

@@ -8,22 +8,26 @@
 // O += P^ V, O_hp += P V, l += rowsum(P) (from the high-precision P).
 // The epilogue divides both accumulators by l and stores the log-sum-exp.
 //
-// Mapping onto the MI355X:
-//  * a workgroup of 4 waves owns 128 query rows (32 per wave); each wave
-//    computes S^T = K Q^T with v_mfma_f32_32x32x16, so every lane owns one
-//    query row and 32 of the tile's 64 keys in registers: the row maximum,
-//    the P-quant absmax and the row sum are in-lane reductions plus one
-//    exchange with the lane 32 apart;
-//  * Q^T stays in registers for the whole loop; K and V tiles of 64 keys are
-//    double-buffered through LDS (XOR-swizzled 16-byte chunks);
+// Mapping onto the MI355X (two kernels: the ping-pong fwd_pp_kernel for
+// value or per-token-code inputs, fwd_f8v_kernel for fp8 V codes):
+//  * every wave owns 32 query rows and computes S^T = K Q^T with
+//    v_mfma_f32_32x32x16, so every lane owns one query row and 32 of the
+//    tile's 64 keys in registers: the row maximum, the P-quant absmax and
+//    the row sum are in-lane reductions plus one exchange with the lane 32
+//    apart;
+//  * K and V tiles of 64 keys are double-buffered through LDS (XOR-swizzled
+//    16-byte chunks), copied HBM -> LDS by DMA;
 //  * O^T = V^T P^T: the P registers are already in the B-operand layout, V^T
-//    comes from LDS through ds_read_b64_tr_b16; the quantized and the
-//    straight-through P@V share that V operand;
+//    comes from LDS through transposing reads; the quantized and the
+//    straight-through P@V share that V operand (with fp8 V the quantized one
+//    runs on the fp8 MFMA from the codes of P^ and V);
 //  * the accumulators are rescaled only when the running maximum grows by
 //    more than 2^8 (exact in real arithmetic: every tile is scaled by the
 //    same stale maximum, and the P-quant absmax scaling is invariant to it).
 #include "common.hpp"
 #include "launch.hpp"
+
+#include <type_traits>
 
 namespace qat {
 
@@ -45,17 +49,34 @@ constexpr int FWD_BM = 128;      // query rows per workgroup
 constexpr int FWD_BN = 64;       // keys per tile (= P_GROUP)
 constexpr float RESCALE_SLACK = 8.0f;
 
-template <class DT, int D, bool CAUSAL, int PQ, int IN>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
-  constexpr bool VFP8 = IN == IN_VFP8;
-  constexpr bool QKS = IN == IN_QKS;
-  constexpr int CH = D / 8;                 // 16-byte chunks per row
-  constexpr int TILE = FWD_BN * D * 2;      // bytes per K or V tile
-  constexpr int LPT = FWD_BN * CH / 256;    // chunks per thread per tile
+// ---------------------------------------------------------------------------
+// Forward with fp8 V: e5m2 codes [B,H,Nkv,D] and a per-(b, h, d) scale.
+//
+// V never leaves its 8-bit codes: tiles go HBM -> LDS by DMA and are read
+// back with ds_read_b64_tr_b8 as V^T operands; v_scale[d] factors out of
+// every key contraction and is applied in the epilogue.
+//  * O (P quant on): P^ = code_P * s, so per tile and column block one
+//    32x32x64 fp8 MFMA of the V codes with the P^ codes forms the exact code
+//    products, and the row's group scale s multiplies the result;
+//  * O_hp: 32x32x16 fp16 MFMAs of P_hp (rounded to fp16) with the same V
+//    operand bytes, widened to fp16 exactly (an e5m2 code is the high byte of
+//    the equal fp16).
+// Four waves own 32 query rows each; Q rows are held in registers as the B
+// operand of S^T = K Q^T; K (bf16) and V tiles are double-buffered in
+// separate LDS arrays selected at compile time, so the reads of one buffer
+// never wait for the copies into the other.
+template <int D, bool CAUSAL, int PQ>
+__global__ __launch_bounds__(256, 2) void fwd_f8v_kernel(FwdArgs a) {
+  using DT = BF16;
+  constexpr int TILE = FWD_BN * D * 2;      // bytes per K tile
+  constexpr int VTILE = FWD_BN * D;         // bytes per V code tile
   constexpr int NDB = D / 32;               // 32-wide d blocks
   constexpr int NKS = D / 16;               // 16-deep k steps over D
-  __shared__ __attribute__((aligned(16))) char smem[2][2][TILE];
-  __shared__ __attribute__((aligned(16))) float ks_s[2][FWD_BN];   // IN_QKS: key scales of the tile
+  constexpr int FQF = PQ >= 0 ? PQ : 0;
+  __shared__ __attribute__((aligned(16))) char k_s0[TILE];
+  __shared__ __attribute__((aligned(16))) char k_s1[TILE];
+  __shared__ __attribute__((aligned(16))) char v_s0[VTILE];
+  __shared__ __attribute__((aligned(16))) char v_s1[VTILE];
 
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int ntq = (a.Nq + FWD_BM - 1) / FWD_BM;
@@ -68,7 +89,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const int Nq = a.Nq, Nkv = a.Nkv;
   const uint16_t* qp = (const uint16_t*)a.q + (size_t)bh * Nq * D;
   const uint16_t* kp = (const uint16_t*)a.k + (size_t)bh * Nkv * D;
-  const uint8_t* vp8 = (const uint8_t*)a.v + (size_t)bh * Nkv * D * (VFP8 ? 1 : 2);
+  const uint8_t* vp = (const uint8_t*)a.v + (size_t)bh * Nkv * D;
+  const float c_row = a.c;
 
   // Q^T operand: lane holds row qi, d = 16ks + 8g .. +7
   s16x8 qf[NKS];
@@ -78,57 +100,18 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     else qf[ks] = (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
   }
 
-  // IN_QKS: S = s_q[i] s_k[j] (code_q . code_k); s_q folds into the log2 scale
-  float c_row = a.c;
-  if constexpr (QKS) c_row = a.c * (qi < Nq ? a.q_scale[(size_t)bh * Nq + qi] : 1.0f);
-  const float* ksp = QKS ? a.k_scale + (size_t)bh * Nkv : nullptr;
-
   const int kv_end = CAUSAL ? min(Nkv, qb + FWD_BM) : Nkv;
   const int ntiles = (kv_end + FWD_BN - 1) / FWD_BN;
-
-  // V codes of the fp8-V path take a register detour (decoded to bf16 on the
-  // way into LDS); every other tile goes HBM -> LDS directly.
-  u32x2 vcode[LPT];
-  float ksreg = 0.0f;
-  TileCopy<D, FWD_BN, 4> copy;
-  copy.init(w, lane);
-  auto issue_tile = [&](int t, int buf) {
-    copy.issue(smem[buf][0], kp, t * FWD_BN, Nkv);
-    if constexpr (VFP8) {
-#pragma unroll
-      for (int u = 0; u < LPT; ++u) {
-        const int idx = tid + 256 * u, row = idx / CH, ch = idx % CH;
-        const int key = min(t * FWD_BN + row, Nkv - 1);
-        vcode[u] = *reinterpret_cast<const u32x2*>(vp8 + (size_t)key * D + ch * 8);
-      }
-    } else {
-      copy.issue(smem[buf][1], (const uint16_t*)vp8, t * FWD_BN, Nkv);
-    }
-    if constexpr (QKS) {
-      const int key = t * FWD_BN + tid;
-      if (tid < FWD_BN) ksreg = key < Nkv ? ksp[key] : 0.0f;
-    }
-  };
-  // register-staged parts of a tile: written after the loads landed
-  auto finish_tile = [&](int buf) {
-    if constexpr (VFP8) {
-#pragma unroll
-      for (int u = 0; u < LPT; ++u) {
-        const int idx = tid + 256 * u, row = idx / CH, ch = idx % CH;
-        u32x4 vv;   // e5m2 codes -> bf16 (exact: every e5m2 value is a bf16 value)
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const uint32_t word = vcode[u][h >> 1] >> (16 * (h & 1));
-          const f32x2 f = __builtin_amdgcn_cvt_pk_f32_bf8((int)word, false);
-          vv[h] = BF16::pack2(f[0], f[1]);
-        }
-        *reinterpret_cast<u32x4*>(smem[buf][1] + tile_off<D>(row, ch)) = vv;
-      }
-    }
-    if constexpr (QKS) {
-      if (tid < FWD_BN) ks_s[buf][tid] = ksreg;
-    }
-  };
+  TileCopy<D, FWD_BN, 4> kcopy;
+  CodeCopy<D, FWD_BN, 4> vcopy;
+  kcopy.init(w, lane);
+  vcopy.init(w, lane);
+  // per-lane parts of the LDS operand addresses (tile_off and vc_off with
+  // the tile-independent terms folded): K row l32, and the V-code row and
+  // 8-byte half of lds_vcode_tr
+  const int vrow = 8 * ((lane & 15) >> 3) + 4 * g + ((lane & 15) >> 1 & 3);
+  const int k_off0 = l32 * (D * 2), k_sw0 = swz<D>(l32);
+  const int v_off0 = vrow * D + ((lane & 1) << 3), v_sw0 = vc_swz<D>(vrow), v_c16 = (lane >> 4) & 1;
 
   float m_used = -INFINITY;   // stale running maximum (scaled log2 units)
   float l_part = 0.0f;        // this lane's share of the row sum
@@ -139,21 +122,22 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     oh_acc[db] = (f32x16){};
   }
 
-  if (ntiles > 0) {
-    issue_tile(0, 0);
-    wait_vmem();
-    finish_tile(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
+  // one tile from buffer BUF (compile-time), copies of the next into the other
+  auto tile_step = [&](auto BUF, int t) __attribute__((always_inline)) {
+    constexpr int bsel = decltype(BUF)::value;
+    char* Kt = bsel ? k_s1 : k_s0;
+    char* Vc = bsel ? v_s1 : v_s0;
+    // recomputed per tile rather than kept live across the loop (which
+    // spills them, and every reload would then wait for the tile copies)
+    int k_off = k_off0, k_sw = k_sw0, v_off = v_off0, v_sw = v_sw0;
+    asm volatile("" : "+v"(k_off), "+v"(k_sw), "+v"(v_off), "+v"(v_sw));
+    if (t + 1 < ntiles) {
+      kcopy.issue(bsel ? k_s0 : k_s1, kp, (t + 1) * FWD_BN, Nkv);
+      vcopy.issue(bsel ? v_s0 : v_s1, vp, (t + 1) * FWD_BN, Nkv);
+    }
     const int kv0 = t * FWD_BN;
     const bool active = (q0 < Nq) && (!CAUSAL || kv0 <= q0 + 31);
     if (active) {
-      const char* Kt = smem[buf][0];
-      const char* Vt = smem[buf][1];
       // ---- S^T = K Q^T (two 32-key blocks)
       prio_mfma();
       f32x16 s[2];
@@ -162,21 +146,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         s[kb] = (f32x16){};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-          const s16x8 ka = lds_row8<D>(Kt, kb * 32 + l32, 2 * ks + g);
+          const s16x8 ka = *reinterpret_cast<const s16x8*>(Kt + kb * 32 * (D * 2) + k_off + (((2 * ks + g) ^ k_sw) << 4));
           s[kb] = DT::mfma(ka, qf[ks], s[kb]);
         }
       }
       prio_valu();
-      if constexpr (QKS) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const f32x4 sk = *reinterpret_cast<const f32x4*>(&ks_s[buf][kb * 32 + 8 * u + 4 * g]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) s[kb][4 * u + e] *= sk[e];
-          }
-      }
       // ---- masks: key tail, causal diagonal
       const bool need_mask = (kv0 + FWD_BN > Nkv) || (CAUSAL && kv0 + FWD_BN - 1 > q0);
       if (need_mask) {
@@ -202,8 +176,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         const float alpha = resc ? fast_exp2(m_used - m_new) : 1.0f;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          o_acc[db] *= alpha;
-          if constexpr (PQ >= 0) oh_acc[db] *= alpha;
+          if constexpr (PQ >= 0) o_acc[db] *= alpha;
+          oh_acc[db] *= alpha;
         }
         l_part *= alpha;
         m_used = m_new;
@@ -214,52 +188,70 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       FqScale fs = {0.0f, 0.0f};
       if constexpr (PQ >= 0) {
         const float pmax = (mx == -INFINITY) ? 0.0f : fast_exp2(__builtin_fmaf(mx, c_row, -m_sub));
-        fs = fq_scale(pmax, Fp8Fmt<(PQ >= 0 ? PQ : 0)>::FMAX);
+        fs = fq_scale(pmax, Fp8Fmt<FQF>::FMAX);
       }
-      // ---- p = exp2(S*c - m)
-      float p[2][16];
+      // ---- p = exp2(S*c - m); operands: P^ codes (dword 4kb + u = keys
+      // 32kb + 8u + 4g + 0..3) and P_hp in fp16 (k step kk = 2kb + h)
       float psum = 0.0f;
+      i32x8 pcode;
+      uint32_t phw[4][4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c_row, -m_sub));
-          psum += p[kb][r];
+          p[r] = fast_exp2(__builtin_fmaf(s[kb][r], c_row, -m_sub));
+          psum += p[r];
         }
-      l_part += psum;
-      // ---- O^T += V^T P^T  (4 k-steps of 16 keys)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int kb = kk >> 1, h = kk & 1;
-        uint32_t ph[4], pq[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) ph[jj] = DT::pack2(p[kb][8 * h + 2 * jj], p[kb][8 * h + 2 * jj + 1]);
         if constexpr (PQ >= 0) {
-          const FqScale f4[4] = {fs, fs, fs, fs};
 #pragma unroll
-          for (int jq = 0; jq < 2; ++jq) {
-            const f32x4 xq = fq_quad<(PQ >= 0 ? PQ : 0)>(&p[kb][8 * h + 4 * jq], f4);
-            pq[2 * jq] = DT::pack2(xq[0], xq[1]);
-            pq[2 * jq + 1] = DT::pack2(xq[2], xq[3]);
-          }
+          for (int u = 0; u < 4; ++u) pcode[4 * kb + u] = fq_codes4<FQF>(&p[4 * u], fs.r);
         }
-        const s16x8 bh_op = __builtin_bit_cast(s16x8, (u32x4){ph[0], ph[1], ph[2], ph[3]});
-        s16x8 bq_op = bh_op;
-        if constexpr (PQ >= 0) bq_op = __builtin_bit_cast(s16x8, (u32x4){pq[0], pq[1], pq[2], pq[3]});
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const s16x8 va = lds_tr8<D>(Vt, kk * 16, db * 32, lane);
-          o_acc[db] = DT::mfma(va, bq_op, o_acc[db]);
-          if constexpr (PQ >= 0) oh_acc[db] = DT::mfma(va, bh_op, oh_acc[db]);
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) phw[2 * kb + h][jj] = FP16::pack2(p[8 * h + 2 * jj], p[8 * h + 2 * jj + 1]);
+      }
+      l_part += psum;
+      // ---- O^T += s (V^T codes . P^ codes^T);  O_hp^T += V^T P_hp^T
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        // lds_vcode_tr with the lane terms precomputed
+        i32x8 vc;
+        const char* vb = Vc + v_off + (((2 * db + v_c16) ^ v_sw) << 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const i32x2 t2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vb + (32 * (r >> 1) + 16 * (r & 1)) * D));
+          vc[2 * r] = t2[0];
+          vc[2 * r + 1] = t2[1];
+        }
+        if constexpr (PQ >= 0) {
+          const f32x16 t8 = mfma_f8_bf8a<FQF>(vc, pcode, (f32x16){});
+          o_acc[db] += t8 * fs.s;
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const s16x8 bop = __builtin_bit_cast(s16x8, (u32x4){phw[kk][0], phw[kk][1], phw[kk][2], phw[kk][3]});
+          oh_acc[db] = FP16::mfma(e5m2x8_to_f16(vc[2 * kk], vc[2 * kk + 1]), bop, oh_acc[db]);
         }
       }
     }
     wait_vmem();
-    if (t + 1 < ntiles) finish_tile(buf ^ 1);
     __syncthreads();
+  };
+
+  if (ntiles > 0) {
+    kcopy.issue(k_s0, kp, 0, Nkv);
+    vcopy.issue(v_s0, vp, 0, Nkv);
+  }
+  wait_vmem();
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    tile_step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < ntiles) tile_step(std::integral_constant<int, 1>{}, t + 1);
   }
 
-  // ---- epilogue
+  // ---- epilogue: O = O_acc / l * v_scale[d] (O_hp likewise)
   if (q0 >= Nq) return;
   const float l = l_part + shfl_xor32(l_part);
   const float inv_l = 1.0f / l;
@@ -271,16 +263,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int d = db * 32 + 8 * u + 4 * g;
-        float vs[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-        if constexpr (VFP8) {
-          const f32x4 sc = *reinterpret_cast<const f32x4*>(a.v_scale + (size_t)bh * D + d);
-          vs[0] = sc[0]; vs[1] = sc[1]; vs[2] = sc[2]; vs[3] = sc[3];
-        }
+        const f32x4 vs = *reinterpret_cast<const f32x4*>(a.v_scale + (size_t)bh * D + d);
         float x[4], y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          x[e] = o_acc[db][4 * u + e] * inv_l * vs[e];
-          y[e] = (PQ >= 0 ? oh_acc[db][4 * u + e] : o_acc[db][4 * u + e]) * inv_l * vs[e];
+          y[e] = oh_acc[db][4 * u + e] * inv_l * vs[e];
+          x[e] = PQ >= 0 ? o_acc[db][4 * u + e] * inv_l * vs[e] : y[e];
         }
         *reinterpret_cast<u32x2*>(op + (size_t)qi * D + d) = (u32x2){DT::pack2(x[0], x[1]), DT::pack2(x[2], x[3])};
         *reinterpret_cast<u32x2*>(ohp + (size_t)qi * D + d) = (u32x2){DT::pack2(y[0], y[1]), DT::pack2(y[2], y[3])};
@@ -310,7 +298,7 @@ constexpr int PP_BM = 256;
 
 template <class DT, int D, bool CAUSAL, int PQ, int IN>
 __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
-  static_assert(IN != IN_VFP8, "fp8 V uses fwd_kernel");
+  static_assert(IN != IN_VFP8, "fp8 V uses fwd_f8v_kernel");
   constexpr bool QKS = IN == IN_QKS;
   constexpr int TILE = FWD_BN * D * 2;
   constexpr int NDB = D / 32;
@@ -592,7 +580,7 @@ template <class DT, int D, bool CAUSAL, int PQ, int IN>
 static hipError_t fwd_launch(const Shape& s, const FwdArgs& a, hipStream_t st) {
   if constexpr (IN == IN_VFP8) {
     dim3 grid(((s.Nq + FWD_BM - 1) / FWD_BM) * s.B * s.H);
-    hipLaunchKernelGGL((fwd_kernel<DT, D, CAUSAL, PQ, IN>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((fwd_f8v_kernel<D, CAUSAL, PQ>), grid, dim3(256), 0, st, a);
   } else {
     dim3 grid(((s.Nq + PP_BM - 1) / PP_BM) * s.B * s.H);
     hipLaunchKernelGGL((fwd_pp_kernel<DT, D, CAUSAL, PQ, IN>), grid, dim3(512), 0, st, a);

@@ -28,6 +28,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int P_GROUP = 64;          // key columns per P-quant scale
 constexpr float LOG2E = 1.4426950408889634f;
@@ -242,6 +244,119 @@ __device__ __forceinline__ f32x4 fq_quad(const float x[4], const FqScale q[4]) {
   }
   return (f32x4){lo[0] * q[0].s, lo[1] * q[1].s, hi[0] * q[2].s, hi[1] * q[3].s};
 }
+
+// The four 8-bit codes of fq_quad (same conversions, byte e = code of x[e]),
+// for callers that feed the codes themselves to an fp8 MFMA.
+template <int FMT>
+__device__ __forceinline__ int fq_codes4(const float x[4], float r) {
+  int pk;
+  if constexpr (FMT == 0) {
+    pk = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] * r, x[1] * r, 0, false);
+    pk = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] * r, x[3] * r, pk, true);
+  } else {
+    pk = __builtin_amdgcn_cvt_pk_bf8_f32(x[0] * r, x[1] * r, 0, false);
+    pk = __builtin_amdgcn_cvt_pk_bf8_f32(x[2] * r, x[3] * r, pk, true);
+  }
+  return pk;
+}
+
+// ---------------------------------------------------------------- fp8 MFMA
+// v_mfma_f32_32x32x64_f8f6f4 with A = e5m2 codes and B = FMT codes (0 e4m3fn,
+// 1 e5m2), unit block scales (E8M0 127).  Operand: 32 bytes per lane; lane l
+// supplies row m (A) or column n (B) = l % 32 and 32 of the 64 k values, the
+// half selected by l / 32.  Any assignment of those 32 k values to bytes works
+// as long as A and B use the same one.  C has the 32x32x16 layout.
+template <int FMT>
+__device__ __forceinline__ f32x16 mfma_f8_bf8a(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 1, FMT, 0, 127, 0, 127);
+}
+
+// LDS tile of 8-bit codes: rows of D bytes in 16-byte chunks, chunk c of row
+// R stored at c ^ vc_swz(R).  The eight rows (R0 + 0..3, R0 + 8..11, R0 a
+// multiple of 4 with bit 3 clear) that one 16-lane transposing read touches
+// then land on eight distinct chunk positions, i.e. distinct banks.
+template <int D>
+__device__ __forceinline__ int vc_swz(int row) {
+  return (((row >> 1) & 1) | (((row >> 3) & 1) << 1) | ((row & 1) << 2)) & (D / 16 - 1);
+}
+// byte offset of the 8-byte half `h8` (0..2D/16-1 over the row) of row `row`
+template <int D>
+__device__ __forceinline__ int vc_off(int row, int h8) {
+  return row * D + (((h8 >> 1) ^ vc_swz<D>(row)) << 4) + ((h8 & 1) << 3);
+}
+
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+// A operand of the fp8 MFMA holding V^T codes for columns 32*db .. +31 of a
+// 64-key code tile: byte j = 8r + s of lane l (column d = 32db + l%32, half
+// g = l/32) is the code of key 32(r/2) + 16(r%2) + 8(s/4) + 4g + s%4, from
+// four ds_read_b64_tr_b8.  Within a 16-lane group that instruction hands
+// lane i, slot s, byte i%8 of the 8 bytes read by lane 2s + i/8; so lane
+// 2s + b of the group reads that key's row at 8-byte half 4db + 2((l/16)%2) + b.
+// The matching B operand holds in dword 4kb + u, bytes e = 0..3, the codes of
+// keys 32kb + 8u + 4g + e: the keys a query lane owns in the S^T layout.
+// Dwords 2r, 2r+1 alone are the 16-deep k step r in the permuted k order of
+// the 16-bit MFMAs (element j = slot j).
+template <int D>
+__device__ __forceinline__ i32x8 lds_vcode_tr(const char* tile, int db, int lane) {
+  const int G = lane >> 4, L = lane & 15, g = lane >> 5, s = L >> 1;
+  const int h8 = 4 * db + 2 * (G & 1) + (L & 1);
+  i32x8 out;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 32 * (r >> 1) + 16 * (r & 1) + 8 * (s >> 2) + 4 * g + (s & 3);
+    const i32x2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(tile + vc_off<D>(row, h8)));
+    out[2 * r] = t[0];
+    out[2 * r + 1] = t[1];
+  }
+  return out;
+}
+
+// Eight e5m2 codes (two dwords, byte j = element j) -> eight fp16 values:
+// an e5m2 code is the high byte of the fp16 with the same value.
+__device__ __forceinline__ s16x8 e5m2x8_to_f16(int lo, int hi) {
+  const uint32_t a = __builtin_amdgcn_perm(lo, lo, 0x010c000cu), b = __builtin_amdgcn_perm(lo, lo, 0x030c020cu);
+  const uint32_t c = __builtin_amdgcn_perm(hi, hi, 0x010c000cu), d = __builtin_amdgcn_perm(hi, hi, 0x030c020cu);
+  return __builtin_bit_cast(s16x8, (u32x4){a, b, c, d});
+}
+
+// Asynchronous copy of [BN x D] 8-bit code tiles from HBM into the vc_swz
+// layout (global_load_lds_dwordx4; same scheme as TileCopy).
+template <int D, int BN, int NW>
+struct CodeCopy {
+  static constexpr int CPR = D / 16;                   // 16-byte chunks per row
+  static constexpr int ROWS_PER_KIB = 1024 / D;
+  static constexpr int KIB = BN * D / 1024;
+  static constexpr int PER_WAVE = KIB / NW;
+  static_assert(KIB % NW == 0, "tile must split evenly over the waves");
+  uint32_t off[PER_WAVE];
+  int wave;
+
+  __device__ __forceinline__ void init(int wave_uniform, int lane) {
+    wave = wave_uniform;
+#pragma unroll
+    for (int u = 0; u < PER_WAVE; ++u) {
+      const int row = (wave * PER_WAVE + u) * ROWS_PER_KIB + lane / CPR;
+      const int chunk = (lane % CPR) ^ vc_swz<D>(row);
+      off[u] = (uint32_t)(row * D + chunk * 16);
+    }
+  }
+  __device__ __forceinline__ void issue(char* lds_tile, const uint8_t* src, int row0, int nrows) const {
+    const char* base = reinterpret_cast<const char*>(src + (size_t)row0 * D);
+    const bool full = row0 + BN <= nrows;
+#pragma unroll
+    for (int u = 0; u < PER_WAVE; ++u) {
+      uint32_t o = off[u];
+      if (!full) {
+        const int row = (int)(o / D);
+        const int r = min(row0 + row, nrows - 1) - row0;
+        o = (uint32_t)(r * D) + (o % D);
+      }
+      __builtin_amdgcn_global_load_lds((const void*)(base + o),
+                                       (lds_void*)(lds_tile + (wave * PER_WAVE + u) * 1024), 16, 0, 0);
+    }
+  }
+};
 
 // ---------------------------------------------------------------- work order
 // MI355X deals the workgroups of a launch to its 8 XCDs round-robin by linear
