@@ -26,6 +26,7 @@ import sys
 import time
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "QAT attn fwd+bwd TFLOP/s, B1 H24 N4608 D128 bf16; % of MFMA peak"
 
@@ -237,7 +238,9 @@ def main():
         "dkdv_kernel": (lambda: bwd(ops.QAT_BWD_DKDV), 8.0 * Wn),
     }
     if w.qkv_quant:
+        # the forward call also runs the Q/K/V pre-pass: time that stage alone
         kernels = {n: kv for n, kv in kernels.items() if n != "fwd_kernel"}
+        kernels["token_quant_kernel"] = (lambda: bwd(ops.QAT_BWD_PREPARE), None)
     kernel_ms = {}
     for name, (fn, _) in kernels.items():
         fn()
@@ -254,6 +257,14 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(dom_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(dom), "kernel": dom,
                 "kernel_ms": {n: round(t, 4) for n, t in kernel_ms.items()}}
+    # HBM-bound stages: algorithmic bytes (each tensor once) per call / duration
+    e = 2
+    BH = w.B * w.H
+    hbm_bytes = {"delta_kernel": BH * w.Nq * (2 * w.D * e + 4)}
+    if w.qkv_quant:   # read Q, K, V; write the Q, K code values, V^ and the Q, K scales
+        hbm_bytes["token_quant_kernel"] = BH * (2 * (w.Nq + 2 * w.Nkv) * w.D * e + 4 * (w.Nq + w.Nkv))
+    roofline["hbm_stages_gbps"] = {n: round(b / (kernel_ms[n] * 1e-3) / 1e9, 1) for n, b in hbm_bytes.items()
+                                   if n in kernel_ms}
 
     # ---- plain copy of a known size (counter calibration runs)
     if args.copy_mib > 0:
@@ -285,6 +296,14 @@ def main():
                "sample": f"{nh} of {w.B * w.H} heads, forward + backward, float64 NumPy, {c1 - c0:.1f} s"}
 
     fa_conv = 14.0 * Wn / (ms_step * 1e-3) / 1e12
+    extra = {}
+    if w.v_fp8:
+        # the quantized P^V runs on the fp8 MFMA (twice the bf16 rate): the
+        # step's time at a blended peak, and the forward's HBM rate (V 1 B/elt)
+        t_peak = (14.0 * Wn / PEAK_BF16_TFLOPS + 2.0 * Wn / PEAK_FP8_TFLOPS) / 1e12
+        extra["pct_of_blended_peak"] = round(100 * t_peak / (ms_step * 1e-3), 2)
+        fwd_bytes = w.B * w.H * (w.Nq * w.D * 2 + w.Nkv * w.D * 2 + w.Nkv * w.D + 2 * w.Nq * w.D * 2 + 4 * w.Nq)
+        extra["fwd_hbm_gbps"] = round(fwd_bytes / (split_ms["fwd"]["median"] * 1e-3) / 1e9, 1)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -303,7 +322,7 @@ def main():
                                f"{', Q/K/V fake-quant e4m3' if w.qkv_quant else ''}"
                                f"{', V e5m2' if w.v_fp8 else ''}",
                    "credited_flop_per_step": credited, "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-                   "fa_convention_tflops": round(fa_conv, 2), "call_ms": split_ms},
+                   "fa_convention_tflops": round(fa_conv, 2), "call_ms": split_ms, **extra},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernel_source_hash": kernel_source_hash(),

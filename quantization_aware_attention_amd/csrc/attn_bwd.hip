@@ -119,11 +119,12 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int ntq = (a.Nq + DQ_BM - 1) / DQ_BM;
-  const int unit = xcd_unit(blockIdx.x, gridDim.x);
-  const int bh = unit / ntq;
-  const int qb = (CAUSAL ? ntq - 1 - unit % ntq : unit % ntq) * DQ_BM;
+  int bh, rank;   // causal: the longest rows (last blocks) first
+  work_unit(blockIdx.x, gridDim.x, ntq, CAUSAL, &bh, &rank);
+  const int qb = (CAUSAL ? ntq - 1 - rank : rank) * DQ_BM;
   const int q0 = qb + w * 32;
   const int qi = q0 + l32;
+  const int lane_g4 = 4 * g, lane_dq = 4 * g - l32;   // mask terms (key - kv0 - c, key - qi + q0 - kv0 - c)
   const int Nq = a.Nq, Nkv = a.Nkv;
   const uint16_t* qp = (const uint16_t*)a.q + (size_t)bh * Nq * D;
   const uint16_t* dop = (const uint16_t*)a.dout + (size_t)bh * Nq * D;
@@ -141,7 +142,9 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   const float Mi = qi < Nq ? a.lse[(size_t)bh * Nq + qi] * LOG2E : 0.0f;
   const float Di = qi < Nq ? a.delta[(size_t)bh * Nq + qi] : 0.0f;
   float c_row = a.c;   // IN_QKS: s_q folds into the log2 scale (same rounding as dK/dV)
-  if constexpr (QKS) c_row = a.c * (qi < Nq ? a.q_scale[(size_t)bh * Nq + qi] : 1.0f);
+  // (a zero scale, all-zero row, is raised to the smallest normal so that a
+  // masked score stays -inf after the product)
+  if constexpr (QKS) c_row = a.c * fmaxf(qi < Nq ? a.q_scale[(size_t)bh * Nq + qi] : 1.0f, 1.17549435e-38f);
 
   f32x16 dq_acc[NDB];
 #pragma unroll
@@ -229,6 +232,9 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
           for (int e = 0; e < 4; ++e) s[kb][4 * u + e] *= v4[e];
         }
     }
+    // masks (key tail, causal diagonal) zero p.  With key = kv0 + c + 4g (c
+    // the element's offset) and qi = q0 + l32, each test compares one
+    // per-lane value with a wave-uniform bound.
     float p[2][16];
     float pmax = 0.0f;
 #pragma unroll
@@ -237,8 +243,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
       for (int r = 0; r < 16; ++r) {
         float x = fast_exp2(__builtin_fmaf(s[kb][r], c_row, -Mi));
         if (need_mask) {
-          const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key >= Nkv || (CAUSAL && key > qi)) x = 0.0f;
+          const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
+          if (lane_g4 >= Nkv - kv0 - c || (CAUSAL && lane_dq > q0 - kv0 - c)) x = 0.0f;
         }
         p[kb][r] = x;
         pmax = fmaxf(pmax, x);
@@ -341,7 +347,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
   // n_split query ranges of the last key blocks, which would otherwise run
   // alone in a last, mostly idle round of the chip.
   int unit, part = 0, nparts = 1;
-  if ((int)blockIdx.x < a.n_whole) {
+  if (CAUSAL) {   // never split; key block 0 sees every query: longest first
+    int bh_c, rank;
+    work_unit(blockIdx.x, gridDim.x, nkb, true, &bh_c, &rank);
+    unit = bh_c * nkb + rank;
+  } else if ((int)blockIdx.x < a.n_whole) {
     unit = xcd_unit(blockIdx.x, a.n_whole);
   } else {
     const int j = xcd_unit(blockIdx.x - a.n_whole, gridDim.x - a.n_whole);
@@ -350,7 +360,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
     nparts = a.n_split;
   }
   const int bh = unit / nkb;
-  const int k0 = (unit % nkb) * DSP_BN;   // causal: key block 0 sees every query: longest first
+  const int k0 = (unit % nkb) * DSP_BN;
   const int k0w = k0 + w * 32;
   const int kj = k0w + l32;
   const int Nq = a.Nq, Nkv = a.Nkv;

@@ -80,10 +80,9 @@ __global__ __launch_bounds__(256, 2) void fwd_f8v_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int ntq = (a.Nq + FWD_BM - 1) / FWD_BM;
-  const int unit = xcd_unit(blockIdx.x, gridDim.x);
-  const int bh = unit / ntq;
-  // causal: the longest rows first, so short tiles fill the tail of the launch
-  const int qb = (CAUSAL ? ntq - 1 - unit % ntq : unit % ntq) * FWD_BM;
+  int bh, rank;   // causal: the longest rows (last blocks) first
+  work_unit(blockIdx.x, gridDim.x, ntq, CAUSAL, &bh, &rank);
+  const int qb = (CAUSAL ? ntq - 1 - rank : rank) * FWD_BM;
   const int q0 = qb + w * 32;
   const int qi = q0 + l32;
   const int Nq = a.Nq, Nkv = a.Nkv;
@@ -314,9 +313,9 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int grp = w >> 2;
   const int ntq = (a.Nq + PP_BM - 1) / PP_BM;
-  const int unit = xcd_unit(blockIdx.x, gridDim.x);
-  const int bh = unit / ntq;
-  const int qb = (CAUSAL ? ntq - 1 - unit % ntq : unit % ntq) * PP_BM;
+  int bh, rank;   // causal: the longest rows (last blocks) first
+  work_unit(blockIdx.x, gridDim.x, ntq, CAUSAL, &bh, &rank);
+  const int qb = (CAUSAL ? ntq - 1 - rank : rank) * PP_BM;
   const int q0 = qb + w * 32;
   const int qi = q0 + l32;
   const int Nq = a.Nq, Nkv = a.Nkv;

@@ -371,6 +371,27 @@ __device__ __forceinline__ int xcd_unit(int linear, int total) {
   return x * base + min(x, rem) + idx;
 }
 
+// Work order of a launch over BH (batch, head) pairs x nblk blocks per pair.
+// Equal blocks (non-causal): xcd_unit's XCD-contiguous, head-major order, so
+// the blocks of one head share an L2.  Causal blocks differ in length up to
+// nblk-fold, and greedy dispatch of a head-by-head sequence can start long
+// blocks last; they are ordered longest first across the whole launch (all
+// heads' longest blocks, then the next longest, ...), and the round-robin
+// dealing of workgroups to XCDs mixes the lengths on every XCD.
+// Sets the head and the block's rank (causal: 0 = longest).
+__device__ __forceinline__ void work_unit(int linear, int total, int nblk, bool longest_first, int* bh,
+                                          int* rank) {
+  if (longest_first) {
+    const int nbh = total / nblk;
+    *bh = linear % nbh;
+    *rank = linear / nbh;
+  } else {
+    const int unit = xcd_unit(linear, total);
+    *bh = unit / nblk;
+    *rank = unit % nblk;
+  }
+}
+
 // ---------------------------------------------------------------- misc
 __device__ __forceinline__ float shfl_xor32(float x) {
   return __shfl_xor(x, 32, 64);
