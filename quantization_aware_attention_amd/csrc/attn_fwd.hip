@@ -304,7 +304,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   constexpr int NKS = D / 16;
   constexpr int FQF = PQ >= 0 ? PQ : 0;
   constexpr int NPV = 4 * NDB;   // P@V steps of an MFMA phase
-  constexpr int PP_AHEAD = QKS ? 2 : 6;   // fragments in flight ahead of their MFMAs (key scales need registers)
+  constexpr int PP_AHEAD = 6;   // fragments in flight ahead of their MFMAs
   __shared__ __attribute__((aligned(16))) char kbuf[2][TILE];
   __shared__ __attribute__((aligned(16))) char vbuf[2][TILE];
   __shared__ __attribute__((aligned(16))) float ks_s[2][FWD_BN];   // IN_QKS: key scales of K(t)
@@ -420,7 +420,6 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
         step(cur, f);
         __builtin_amdgcn_sched_barrier(0);
       }
-      scale_keys(t);
     } else {          // first and last phases, causal edges: the same steps unpipelined
       if (do_pv) {
 #pragma unroll
@@ -429,12 +428,15 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       if (do_qk) {
 #pragma unroll
         for (int f = NPV; f < NFR; ++f) step(fetch(Vt, Kt, f), f);
-        scale_keys(t);
       }
     }
   };
   auto valu_phase = [&](int t) __attribute__((always_inline)) {
     if (!active(t)) return;
+    // IN_QKS: the key scales of tile t stay in ks_s[t & 1] until group 0's
+    // VALU phase of tile t + 1 rewrites that buffer, after both groups' VALU
+    // phases of tile t
+    scale_keys(t);
     const int kv0 = t * FWD_BN;
     if ((kv0 + FWD_BN > Nkv) || (CAUSAL && kv0 + FWD_BN - 1 > q0)) {
 #pragma unroll
