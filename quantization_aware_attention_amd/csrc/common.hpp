@@ -272,12 +272,14 @@ __device__ __forceinline__ f32x16 mfma_f8_bf8a(const i32x8& a, const i32x8& b, c
 }
 
 // LDS tile of 8-bit codes: rows of D bytes in 16-byte chunks, chunk c of row
-// R stored at c ^ vc_swz(R).  The eight rows (R0 + 0..3, R0 + 8..11, R0 a
-// multiple of 4 with bit 3 clear) that one 16-lane transposing read touches
-// then land on eight distinct chunk positions, i.e. distinct banks.
+// R stored at c ^ vc_swz(R).  A half-wave of transposing reads touches eight
+// rows (R0 + 0..3, R0 + 8..11; R0 a multiple of 4 with bit 3 clear) at two
+// adjacent chunks (2k, 2k + 1); rows of equal parity share a 256-byte bank
+// line, so the four of each parity get the even offsets 0, 2, 4, 6 and their
+// 4 x 2 chunks fall on eight distinct bank groups.
 template <int D>
 __device__ __forceinline__ int vc_swz(int row) {
-  return (((row >> 1) & 1) | (((row >> 3) & 1) << 1) | ((row & 1) << 2)) & (D / 16 - 1);
+  return (2 * (((row >> 1) & 1) | (((row >> 3) & 1) << 1))) & (D / 16 - 1);
 }
 // byte offset of the 8-byte half `h8` (0..2D/16-1 over the row) of row `row`
 template <int D>
