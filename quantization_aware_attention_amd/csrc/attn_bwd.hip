@@ -240,15 +240,23 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = fast_exp2(__builtin_fmaf(s[kb][r], c_row, -Mi));
-        if (need_mask) {
+      for (int r = 0; r < 16; ++r) p[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c_row, -Mi));
+    if (need_mask) {
+      // an opaque statement keeps this a branch: otherwise the masks are
+      // if-converted into selects that every tile executes
+      asm volatile("");
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
           const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
-          if (lane_g4 >= Nkv - kv0 - c || (CAUSAL && lane_dq > q0 - kv0 - c)) x = 0.0f;
+          if (lane_g4 >= Nkv - kv0 - c || (CAUSAL && lane_dq > q0 - kv0 - c)) p[kb][r] = 0.0f;
         }
-        p[kb][r] = x;
-        pmax = fmaxf(pmax, x);
-      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pmax = fmaxf(pmax, p[kb][r]);
     if constexpr (PQ >= 0) {
       pmax = fmaxf(pmax, shfl_xor32(pmax));
       if (g == 0 && qi < Nq) a.p_amax[((size_t)bh * a.NG + t) * Nq + qi] = pmax;
