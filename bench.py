@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dit_image")
     ap.add_argument("--kernel-reps", type=int, default=20)
-    ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the oracle sample (0: skip)")
+    ap.add_argument("--cpu-heads", type=int, default=6, help="heads in the oracle sample (0: skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (calibrates HBM byte counters)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
