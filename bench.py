@@ -55,7 +55,7 @@ KERNEL_TAGS = {
     "delta_kernel": ("delta_kernel",),
     "dq_kernel": ("dq_kernel",),
     "dkdv_kernel": ("dkdv_sp_kernel", "dkdv_merge_kernel"),
-    "token_quant_kernel": ("token_quant_kernel",),
+    "token_quant_kernel": ("token_quant_kernel", "kmean_partial_kernel", "kmean_final_kernel", "shift_rows_kernel"),
 }
 
 
@@ -172,6 +172,7 @@ def main():
     q, k, v, do = up("q"), up("k"), up("v"), up("do")
     flags = ops.QAT_P_QUANT | (ops.QAT_P_E5M2 if w.p_fmt == "e5m2" else 0)
     flags |= ops.QAT_QKV_QUANT if w.qkv_quant else 0
+    flags |= ops.QAT_SMOOTH_K if w.smooth_k else 0
     v_scale = None
     if w.v_fp8:
         flags |= ops.QAT_V_FP8_E5M2
@@ -237,8 +238,8 @@ def main():
         "dq_kernel": (lambda: bwd(ops.QAT_BWD_DQ), 2.0 * Wn),
         "dkdv_kernel": (lambda: bwd(ops.QAT_BWD_DKDV), 8.0 * Wn),
     }
-    if w.qkv_quant:
-        # the forward call also runs the Q/K/V pre-pass: time that stage alone
+    if w.qkv_quant or w.smooth_k:
+        # the forward call also runs the K smoothing / Q/K/V pre-pass: time that stage alone
         kernels = {n: kv for n, kv in kernels.items() if n != "fwd_kernel"}
         kernels["token_quant_kernel"] = (lambda: bwd(ops.QAT_BWD_PREPARE), None)
     kernel_ms = {}
@@ -261,8 +262,13 @@ def main():
     e = 2
     BH = w.B * w.H
     hbm_bytes = {"delta_kernel": BH * w.Nq * (2 * w.D * e + 4)}
+    prep_bytes = 0
+    if w.smooth_k:    # read K for its mean; without Q/K/V quant also read K, write K - mean
+        prep_bytes += BH * w.Nkv * w.D * e * (1 if w.qkv_quant else 3)
     if w.qkv_quant:   # read Q, K, V; write the Q, K code values, V^ and the Q, K scales
-        hbm_bytes["token_quant_kernel"] = BH * (2 * (w.Nq + 2 * w.Nkv) * w.D * e + 4 * (w.Nq + w.Nkv))
+        prep_bytes += BH * (2 * (w.Nq + 2 * w.Nkv) * w.D * e + 4 * (w.Nq + w.Nkv))
+    if prep_bytes:
+        hbm_bytes["token_quant_kernel"] = prep_bytes
     roofline["hbm_stages_gbps"] = {n: round(b / (kernel_ms[n] * 1e-3) / 1e9, 1) for n, b in hbm_bytes.items()
                                    if n in kernel_ms}
 
@@ -286,7 +292,8 @@ def main():
         if w.v_fp8:
             v_codes, vs = oracle.quantize_v_channels(sample["v"], "e5m2")
         c0 = time.perf_counter()
-        kw = dict(causal=w.causal, p_fmt=w.p_fmt, qkv_quant=w.qkv_quant, v_codes=v_codes, v_scale=vs)
+        kw = dict(causal=w.causal, p_fmt=w.p_fmt, qkv_quant=w.qkv_quant, v_codes=v_codes, v_scale=vs,
+                  smooth_k=w.smooth_k, dtype=w.dtype)
         oracle.attention_forward(sample["q"], sample["k"], sample["v"], w.sm_scale, **kw)
         oracle.attention_backward(sample["q"], sample["k"], sample["v"], sample["do"], w.sm_scale, **kw)
         c1 = time.perf_counter()
@@ -319,6 +326,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B{w.B} H{w.H} Nq{w.Nq} Nkv{w.Nkv} D{w.D} {w.dtype}, "
                                f"{'causal' if w.causal else 'non-causal'}, P fake-quant {w.p_fmt}"
+                               f"{', K smoothed' if w.smooth_k else ''}"
                                f"{', Q/K/V fake-quant e4m3' if w.qkv_quant else ''}"
                                f"{', V e5m2' if w.v_fp8 else ''}",
                    "credited_flop_per_step": credited, "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),

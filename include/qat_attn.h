@@ -63,6 +63,19 @@ extern "C" {
 #define QAT_P_E5M2      (1u << 1) /* P grid e5m2 (else e4m3fn)                          */
 #define QAT_QKV_QUANT   (1u << 2) /* per-token e4m3fn fake quant of Q, K, V over D      */
 #define QAT_V_FP8_E5M2  (1u << 3) /* v holds e5m2 codes (uint8) + v_scale[B,H,D] fp32  */
+/*
+ * K smoothing (FastVideo attn_qat_train.py, _attention.forward "smoothing k
+ * from SageAttn", and the SMOOTH_K term of _attn_bwd_dq): k_mean[d], the mean
+ * of K over every batch, head and token rounded to the dtype, is subtracted
+ * from K (rounded to the dtype) before anything else, Q/K/V quantization
+ * included.  Softmax does not change under that per-row score shift, so O,
+ * O_hp and dV are those of the unsmoothed inputs (up to the rounding of
+ * K - k_mean, and the K quantization then differs); lse is that of the
+ * smoothed scores, i.e. shifted by -sm_scale * (q . k_mean).  dQ takes the
+ * term sm_scale * rowsum(dS) k_mean, so it is the gradient for the original
+ * K; dK is returned as computed for the smoothed K.
+ */
+#define QAT_SMOOTH_K    (1u << 4)
 
 #define QAT_ATTN_P_GROUP 64       /* key columns per P-quant scale (absolute columns)   */
 
@@ -125,7 +138,8 @@ int qat_attn_bwd(const qat_attn_dims* dims, const void* q, const void* k, const 
  * The backward as separately launchable stages, for callers that time,
  * interleave or overlap them.  Arguments and workspace are those of
  * qat_attn_bwd; `stages` is a mask of
- *   QAT_BWD_PREPARE  Q/K/V fake quant into the workspace (QAT_QKV_QUANT only)
+ *   QAT_BWD_PREPARE  K smoothing and Q/K/V fake quant into the workspace
+ *                    (QAT_SMOOTH_K, QAT_QKV_QUANT)
  *   QAT_BWD_DELTA    Delta = rowsum(dout o o_hp) into the workspace
  *   QAT_BWD_DQ       dq, and the per-(row, 64-key group) P absmax into the
  *                    workspace (QAT_P_QUANT)

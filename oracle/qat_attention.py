@@ -53,6 +53,14 @@ on the pages):
 * The log-sum-exp is returned in natural-log units (the source keeps base 2).
 * fp8 V (cross-attention case): one scale per (batch, head, channel d) over
   the key axis, e5m2 grid.
+* K smoothing (``_attention.forward``, "smoothing k", and the SMOOTH_K term of
+  ``_attn_bwd_dq``): k_mean[d] is the mean of K over every batch, head and
+  token, rounded to the storage dtype (the source keeps it in K's dtype);
+  K_s = K - k_mean rounded to the dtype replaces K before anything else,
+  Q/K/V quantization included; dQ = sm_scale (dS K^_s + rowsum(dS) k_mean),
+  the gradient for the original K.  dK is the one of the smoothed K.
+  Rounding to the dtype goes through float32 (round to nearest even), then
+  to bf16 (nearest even on the upper 16 bits) or fp16.
 """
 from __future__ import annotations
 
@@ -154,6 +162,32 @@ def dequant_v_channels(codes, v_scale, fmt: str = "e5m2") -> np.ndarray:
 # --------------------------------------------------------------------------
 # Attention, one (b, h) head
 # --------------------------------------------------------------------------
+# --------------------------------------------------------------------------
+# K smoothing
+# --------------------------------------------------------------------------
+def round_storage(x, dtype: str) -> np.ndarray:
+    """float64 values rounded to bf16 or fp16 storage, through float32."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    if dtype == "fp16":
+        return x32.astype(np.float16).astype(np.float64)
+    if dtype != "bf16":
+        raise ValueError(dtype)
+    u = x32.view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def smooth_key_mean(k, dtype: str) -> np.ndarray:
+    """k_mean[d]: the mean of K [B, H, N, D] over batch, heads and tokens,
+    rounded to the dtype."""
+    return round_storage(np.asarray(k, dtype=np.float64).mean(axis=(0, 1, 2)), dtype)
+
+
+def smooth_keys(kh, k_mean, dtype: str) -> np.ndarray:
+    """K_s = K - k_mean, rounded to the dtype."""
+    return round_storage(np.asarray(kh, dtype=np.float64) - k_mean, dtype)
+
+
 def _scores(qh, kh, sm_scale, causal, rows):
     """S for the query rows ``rows`` (absolute indices), causal mask applied."""
     S = float(sm_scale) * (qh[rows] @ kh.T)
@@ -202,11 +236,13 @@ def forward_head(qh, kh, vh, sm_scale, causal=False, p_quant=True, p_fmt="e4m3",
 
 
 def backward_head(qh, kh, vh, do, sm_scale, causal=False, p_quant=True, p_fmt="e4m3",
-                  group=P_GROUP, q_rows=None, k_rows=None, row_block=2048):
+                  group=P_GROUP, q_rows=None, k_rows=None, row_block=2048, k_mean=None):
     """Straight-through backward of one head.
 
     ``do`` is dO [Nq, D].  Returns ``(dQ[q_rows], dK[k_rows], dV[k_rows])``
-    (all rows when None).  The sums over query rows that make dK and dV are
+    (all rows when None).  With ``k_mean`` (K smoothing; ``kh`` is then the
+    smoothed K) dQ takes the term sm_scale rowsum(dS) k_mean.  The sums over
+    query rows that make dK and dV are
     split into row blocks only to bound memory, and only the columns of P
     that the requested keys need are formed (with their whole P-quant group,
     since a group's scale depends on all of its columns); within a block
@@ -242,6 +278,8 @@ def backward_head(qh, kh, vh, do, sm_scale, causal=False, p_quant=True, p_fmt="e
             dP_q = do[r[sel]] @ vh.T
             dS_q = P[sel] * (dP_q - Delta[sel, None])
             dQ[r[sel]] = float(sm_scale) * (dS_q @ kh)        # dQ = scale dS K
+            if k_mean is not None:                            # + scale rowsum(dS) k_mean
+                dQ[r[sel]] += float(sm_scale) * np.sum(dS_q, axis=1)[:, None] * np.asarray(k_mean)[None, :]
     return dQ[q_rows], dK, dV
 
 
@@ -269,9 +307,11 @@ def prepare_inputs(q, k, v, qkv_quant=False, v_codes=None, v_scale=None, heads=N
     return qh, kh, vh
 
 
-def _prepare_head(q, k, v, b, h, qkv_quant, v_codes, v_scale):
+def _prepare_head(q, k, v, b, h, qkv_quant, v_codes, v_scale, k_mean=None, dtype="bf16"):
     qh = np.asarray(q[b, h], dtype=np.float64)
     kh = np.asarray(k[b, h], dtype=np.float64)
+    if k_mean is not None:
+        kh = smooth_keys(kh, k_mean, dtype)
     if qkv_quant:
         qh = quantize_token_rows(qh, "e4m3")[2].astype(np.float64)
         kh = quantize_token_rows(kh, "e4m3")[2].astype(np.float64)
@@ -286,7 +326,7 @@ def _prepare_head(q, k, v, b, h, qkv_quant, v_codes, v_scale):
 
 def attention_forward(q, k, v, sm_scale, causal=False, p_quant=True, p_fmt="e4m3",
                       qkv_quant=False, v_codes=None, v_scale=None, group=P_GROUP,
-                      heads=None, rows=None):
+                      heads=None, rows=None, smooth_k=False, dtype="bf16"):
     """Forward over [B, H, N, D] inputs.
 
     Returns ``(O, O_hp, lse)`` with shapes [B, H, Nq, D] and [B, H, Nq] (only
@@ -299,8 +339,9 @@ def attention_forward(q, k, v, sm_scale, causal=False, p_quant=True, p_fmt="e4m3
     O = np.zeros((B, H, nr, D))
     O_hp = np.zeros_like(O)
     lse = np.zeros((B, H, nr))
+    k_mean = smooth_key_mean(k, dtype) if smooth_k else None
     for b, h in (heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]):
-        qh, kh, vh = _prepare_head(q, k, v, b, h, qkv_quant, v_codes, v_scale)
+        qh, kh, vh = _prepare_head(q, k, v, b, h, qkv_quant, v_codes, v_scale, k_mean, dtype)
         O[b, h], O_hp[b, h], lse[b, h] = forward_head(
             qh, kh, vh, sm_scale, causal, p_quant, p_fmt, group, rows)
     return O, O_hp, lse
@@ -308,7 +349,7 @@ def attention_forward(q, k, v, sm_scale, causal=False, p_quant=True, p_fmt="e4m3
 
 def attention_backward(q, k, v, do, sm_scale, causal=False, p_quant=True, p_fmt="e4m3",
                        qkv_quant=False, v_codes=None, v_scale=None, group=P_GROUP,
-                       heads=None, q_rows=None, k_rows=None):
+                       heads=None, q_rows=None, k_rows=None, smooth_k=False, dtype="bf16"):
     """Straight-through backward over [B, H, N, D]: returns (dQ, dK, dV)."""
     q = np.asarray(q)
     B, H, Nq, D = q.shape
@@ -318,11 +359,12 @@ def attention_backward(q, k, v, do, sm_scale, causal=False, p_quant=True, p_fmt=
     dQ = np.zeros((B, H, nq, D))
     dK = np.zeros((B, H, nk, D))
     dV = np.zeros((B, H, nk, D))
+    k_mean = smooth_key_mean(k, dtype) if smooth_k else None
     for b, h in (heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]):
-        qh, kh, vh = _prepare_head(q, k, v, b, h, qkv_quant, v_codes, v_scale)
+        qh, kh, vh = _prepare_head(q, k, v, b, h, qkv_quant, v_codes, v_scale, k_mean, dtype)
         dQ[b, h], dK[b, h], dV[b, h] = backward_head(
             qh, kh, vh, np.asarray(do[b, h], dtype=np.float64), sm_scale, causal, p_quant, p_fmt,
-            group, q_rows, k_rows)
+            group, q_rows, k_rows, k_mean=k_mean)
     return dQ, dK, dV
 
 

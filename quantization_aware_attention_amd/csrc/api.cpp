@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr uint32_t KNOWN_FLAGS = QAT_P_QUANT | QAT_P_E5M2 | QAT_QKV_QUANT | QAT_V_FP8_E5M2;
+constexpr uint32_t KNOWN_FLAGS = QAT_P_QUANT | QAT_P_E5M2 | QAT_QKV_QUANT | QAT_V_FP8_E5M2 | QAT_SMOOTH_K;
 constexpr size_t ALIGN = 256;
 
 inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
@@ -21,13 +21,15 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 // Workspace layout (each piece 256-byte aligned, in this order):
 //   bwd: delta fp32 [B,H,Nq]; p_amax fp32 [B,H,ceil(Nkv/64),Nq] (P quant only);
 //   fp32 partial dK/dV of key blocks split over query ranges
+//   fwd and bwd, with K smoothing: the mean's partial sums fp32 [256, D], the
+//   mean fp32 [D] and, without Q/K/V quantization, K - mean (dtype);
 //   fwd and bwd, when Q/K/V quantization is on: the fp8 code values of Q and
 //   K (dtype) with their per-token scales (fp32 [B,H,Nq], [B,H,Nkv]), and
 //   V^ = code * scale rounded to the dtype
 qat::Shape shape_of(const qat_attn_dims& d) { return qat::Shape{d.B, d.H, d.Nq, d.Nkv, d.D, d.dtype}; }
 
 struct Layout {
-  size_t delta = 0, amax = 0, part = 0, qh = 0, kh = 0, vh = 0, qs = 0, ks = 0, total = 0;
+  size_t delta = 0, amax = 0, part = 0, kpart = 0, kmean = 0, ksm = 0, qh = 0, kh = 0, vh = 0, qs = 0, ks = 0, total = 0;
 };
 
 Layout layout(const qat_attn_dims& d, uint32_t flags, int pass) {
@@ -44,6 +46,16 @@ Layout layout(const qat_attn_dims& d, uint32_t flags, int pass) {
     }
     L.part = off;
     off += align_up(qat::dkdv_part_bytes(shape_of(d)));
+  }
+  if (flags & QAT_SMOOTH_K) {
+    L.kpart = off;
+    off += align_up((size_t)qat::KMEAN_BLOCKS * d.D * sizeof(float));
+    L.kmean = off;
+    off += align_up((size_t)d.D * sizeof(float));
+    if (!(flags & QAT_QKV_QUANT)) {
+      L.ksm = off;
+      off += align_up(BH * d.Nkv * d.D * 2);
+    }
   }
   if (flags & QAT_QKV_QUANT) {
     L.qh = off;
@@ -101,18 +113,42 @@ int pfmt_of(uint32_t flags) {
 // quantization the pre-pass outputs in the workspace (run here).
 int prepare_inputs(const qat_attn_dims& d, const Layout& L, uint32_t flags, const void* q, const void* k,
                    const void* v, const float* v_scale, char* ws, hipStream_t st, qat::Inputs* in) {
-  *in = qat::Inputs{q, k, v, v_scale, nullptr, nullptr, qat::IN_PLAIN};
+  *in = qat::Inputs{q, k, v, v_scale, nullptr, nullptr, qat::IN_PLAIN, nullptr};
   if (flags & QAT_V_FP8_E5M2) in->mode = qat::IN_VFP8;
+  const long BH = (long)d.B * d.H;
+  float* kmean = nullptr;
+  if (flags & QAT_SMOOTH_K) {   // k_mean, and K - k_mean unless the quant pre-pass subtracts it
+    kmean = reinterpret_cast<float*>(ws + L.kmean);
+    void* ksm = (flags & QAT_QKV_QUANT) ? nullptr : ws + L.ksm;
+    QAT_TRY(qat::launch_k_smooth(d.dtype, d.D, BH * d.Nkv, k, reinterpret_cast<float*>(ws + L.kpart), kmean, ksm, st));
+    in->k_mean = kmean;
+    if (ksm) in->k = ksm;
+  }
   if (flags & QAT_QKV_QUANT) {
-    const long BH = (long)d.B * d.H;
     float* qs = reinterpret_cast<float*>(ws + L.qs);
     float* ks = reinterpret_cast<float*>(ws + L.ks);
-    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nq, q, ws + L.qh, qs, st));
-    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nkv, k, ws + L.kh, ks, st));
-    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nkv, v, ws + L.vh, nullptr, st));
-    *in = qat::Inputs{ws + L.qh, ws + L.kh, ws + L.vh, nullptr, qs, ks, qat::IN_QKS};
+    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nq, q, ws + L.qh, qs, nullptr, st));
+    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nkv, k, ws + L.kh, ks, kmean, st));
+    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nkv, v, ws + L.vh, nullptr, nullptr, st));
+    *in = qat::Inputs{ws + L.qh, ws + L.kh, ws + L.vh, nullptr, qs, ks, qat::IN_QKS, kmean};
   }
   return QAT_OK;
+}
+
+// The inputs of the attention stages when the pre-passes ran earlier (their
+// outputs are in the workspace).
+qat::Inputs prepared_inputs(const Layout& L, uint32_t flags, const void* q, const void* k, const void* v,
+                            const float* v_scale, char* ws) {
+  qat::Inputs in{q, k, v, v_scale, nullptr, nullptr, qat::IN_PLAIN, nullptr};
+  if (flags & QAT_V_FP8_E5M2) in.mode = qat::IN_VFP8;
+  if (flags & QAT_SMOOTH_K) {
+    in.k_mean = reinterpret_cast<float*>(ws + L.kmean);
+    if (!(flags & QAT_QKV_QUANT)) in.k = ws + L.ksm;
+  }
+  if (flags & QAT_QKV_QUANT)
+    in = qat::Inputs{ws + L.qh, ws + L.kh, ws + L.vh, nullptr, reinterpret_cast<float*>(ws + L.qs),
+                     reinterpret_cast<float*>(ws + L.ks), qat::IN_QKS, in.k_mean};
+  return in;
 }
 
 }  // namespace
@@ -173,11 +209,11 @@ int qat_attn_bwd_stages(const qat_attn_dims* dims, const void* q, const void* k,
   const qat::Shape s = shape_of(d);
   char* ws = static_cast<char*>(workspace);
   qat::Inputs in;
-  const uint32_t prep = (stages & QAT_BWD_PREPARE) ? quant_flags : (quant_flags & ~QAT_QKV_QUANT);
-  if ((rc = prepare_inputs(d, L, prep, q, k, v, v_scale, ws, st, &in)) != QAT_OK) return rc;
-  if (quant_flags & QAT_QKV_QUANT)   // later stages read the prepared inputs
-    in = qat::Inputs{ws + L.qh, ws + L.kh, ws + L.vh, nullptr, reinterpret_cast<float*>(ws + L.qs),
-                     reinterpret_cast<float*>(ws + L.ks), qat::IN_QKS};
+  if (stages & QAT_BWD_PREPARE) {
+    if ((rc = prepare_inputs(d, L, quant_flags, q, k, v, v_scale, ws, st, &in)) != QAT_OK) return rc;
+  } else {   // later stages read what the prepare stage left in the workspace
+    in = prepared_inputs(L, quant_flags, q, k, v, v_scale, ws);
+  }
   float* delta = reinterpret_cast<float*>(ws + L.delta);
   float* amax = (quant_flags & QAT_P_QUANT) ? reinterpret_cast<float*>(ws + L.amax) : nullptr;
   const int pfmt = pfmt_of(quant_flags);

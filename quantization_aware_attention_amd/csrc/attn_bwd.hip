@@ -93,6 +93,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dkdv_part;     // fp32 partial dK/dV of split key blocks
+  const float* k_mean;  // K smoothing: dQ += rowsum(dS) k_mean (null: off)
   int n_whole;          // dK/dV: key blocks run whole by one workgroup each
   int n_split;          // dK/dV: query-range parts of each remaining key block
   int Nq, Nkv, NG;
@@ -105,7 +106,9 @@ struct BwdArgs {
 constexpr int DQ_BM = 128;
 constexpr int DQ_BN = 64;
 
-template <class DT, int D, bool CAUSAL, int PQ, int IN>
+// SMK: K smoothing, dQ += sm_scale rowsum(dS) k_mean (a separate instance, so
+// that the plain kernel is not burdened with the extra row sum)
+template <class DT, int D, bool CAUSAL, int PQ, int IN, bool SMK>
 __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   constexpr bool VFP8 = IN == IN_VFP8;
   constexpr bool QKS = IN == IN_QKS;
@@ -149,6 +152,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   f32x16 dq_acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dq_acc[db] = (f32x16){};
+  constexpr bool smooth = SMK;
+  float ds_rowsum = 0.0f;   // this lane's half of sum_j dS_ij (K smoothing)
 
   // K tiles (and V, unless fp8) go HBM -> LDS directly, double-buffered; fp8
   // V codes and key scales take a register detour.
@@ -261,6 +266,12 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
       pmax = fmaxf(pmax, shfl_xor32(pmax));
       if (g == 0 && qi < Nq) a.p_amax[((size_t)bh * a.NG + t) * Nq + qi] = pmax;
     }
+    if constexpr (smooth) {   // K smoothing: sum_j dS_ij (fp32, before any key scale)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ds_rowsum += p[kb][r] * (dp[kb][r] - Di);
+    }
     // dQ^T += K^T dS^T
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -290,6 +301,9 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   // causal rows whose every later tile was skipped still record zero-free
   // groups only for tiles they visited; the dK/dV kernel never reads the
   // others (the keys are masked there).
+  // K smoothing: dQ is taken for the original K = (K - k_mean) + k_mean
+  float rs = 0.0f;
+  if constexpr (smooth) rs = ds_rowsum + shfl_xor32(ds_rowsum);
   if (qi >= Nq) return;
   uint16_t* dqp = (uint16_t*)a.dq + (size_t)bh * Nq * D;
 #pragma unroll
@@ -297,7 +311,12 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int d = db * 32 + 8 * u + 4 * g;
-      const float x[4] = {dq_acc[db][4 * u], dq_acc[db][4 * u + 1], dq_acc[db][4 * u + 2], dq_acc[db][4 * u + 3]};
+      float x[4] = {dq_acc[db][4 * u], dq_acc[db][4 * u + 1], dq_acc[db][4 * u + 2], dq_acc[db][4 * u + 3]};
+      if constexpr (smooth) {
+        const f32x4 km = *reinterpret_cast<const f32x4*>(a.k_mean + d);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] += rs * km[e];
+      }
       *reinterpret_cast<u32x2*>(dqp + (size_t)qi * D + d) =
           (u32x2){DT::pack2(x[0] * a.sm_scale, x[1] * a.sm_scale), DT::pack2(x[2] * a.sm_scale, x[3] * a.sm_scale)};
     }
@@ -734,7 +753,8 @@ __global__ __launch_bounds__(256) void dkdv_merge_kernel(BwdArgs a, int nkb) {
 template <class DT, int D, bool CAUSAL, int PQ, int IN>
 struct DqK {
   static void run(dim3 g, const BwdArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((dq_kernel<DT, D, CAUSAL, PQ, IN>), g, dim3(256), 0, st, a);
+    if (a.k_mean) hipLaunchKernelGGL((dq_kernel<DT, D, CAUSAL, PQ, IN, true>), g, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((dq_kernel<DT, D, CAUSAL, PQ, IN, false>), g, dim3(256), 0, st, a);
   }
 };
 template <class DT, int D, bool CAUSAL, int PQ, int IN>
@@ -787,6 +807,7 @@ static BwdArgs make_args(const Shape& s, const Inputs& in, const void* dout, con
   a.v_scale = in.v_scale; a.q_scale = in.q_scale; a.k_scale = in.k_scale;
   a.dout = dout; a.lse = lse; a.delta = delta;
   a.Nq = s.Nq; a.Nkv = s.Nkv; a.NG = (s.Nkv + P_GROUP - 1) / P_GROUP;
+  a.k_mean = in.k_mean;
   a.sm_scale = sm_scale;
   a.c = sm_scale * LOG2E;
   return a;

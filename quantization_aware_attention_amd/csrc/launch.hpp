@@ -26,6 +26,7 @@ struct Inputs {
   const float* q_scale;   // IN_QKS
   const float* k_scale;   // IN_QKS
   int mode;
+  const float* k_mean;    // K smoothing: the mean subtracted from K (dQ correction), or null
 };
 
 // pfmt: -1 = P not quantized, 0 = e4m3fn, 1 = e5m2
@@ -35,7 +36,14 @@ hipError_t launch_fwd(const Shape& s, const Inputs& in, float sm_scale, bool cau
 // Per-token e4m3 fake quant: x [rows, D] -> xhat [rows, D] (same dtype); with
 // scale_out the code values and the per-row scales are stored separately.
 hipError_t launch_token_quant(int dtype, int D, long rows, const void* x, void* xhat, float* scale_out,
-                              hipStream_t st);
+                              const float* shift, hipStream_t st);
+
+// K smoothing: mean[D] = dtype-rounded mean of K [rows, D] over all rows
+// (part: KMEAN_BLOCKS x D fp32 scratch); with k_smooth, also K - mean rounded
+// to the dtype.
+constexpr int KMEAN_BLOCKS = 256;
+hipError_t launch_k_smooth(int dtype, int D, long rows, const void* k, float* part, float* mean, void* k_smooth,
+                           hipStream_t st);
 
 // Per-channel e5m2 quant of V [BH, N, D] -> codes [BH, N, D], v_scale [BH, D].
 hipError_t launch_v_quant(int dtype, int D, int BH, int N, const void* v, uint8_t* codes,

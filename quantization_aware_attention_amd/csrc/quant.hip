@@ -17,10 +17,13 @@ namespace qat {
 // split: the fp8 code values (exact in bf16 and fp16) and the fp32 scale s,
 // so that x^ = code * s stays exact for the attention kernels; otherwise
 // x^ = fp32(code * s) is rounded to the storage dtype.
+// With `shift` (K smoothing) the row first becomes x - shift[d], rounded to
+// the dtype: the smoothed K the attention sees.
 template <class DT, int D>
 __global__ __launch_bounds__(256) void token_quant_kernel(const uint16_t* __restrict__ x,
                                                           uint16_t* __restrict__ xhat,
-                                                          float* __restrict__ scale_out, long rows) {
+                                                          float* __restrict__ scale_out, long rows,
+                                                          const float* __restrict__ shift) {
   constexpr int EPL = D / 16;   // elements per lane
   const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
@@ -35,6 +38,10 @@ __global__ __launch_bounds__(256) void token_quant_kernel(const uint16_t* __rest
     const u32x2 w = valid ? *reinterpret_cast<const u32x2*>(src) : (u32x2){0, 0};
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = DT::to_f32((uint16_t)(w[e >> 1] >> (16 * (e & 1))));
+  }
+  if (shift) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) v[e] = DT::to_f32((uint16_t)DT::pack2(v[e] - shift[sub * EPL + e], 0.0f));
   }
   float amax = 0.0f;
 #pragma unroll
@@ -59,17 +66,105 @@ __global__ __launch_bounds__(256) void token_quant_kernel(const uint16_t* __rest
 }
 
 hipError_t launch_token_quant(int dtype, int D, long rows, const void* x, void* xhat, float* scale_out,
-                              hipStream_t st) {
+                              const float* shift, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   dim3 grid((unsigned)((rows + 15) / 16));
   const uint16_t* xi = (const uint16_t*)x;
   uint16_t* xo = (uint16_t*)xhat;
   if (dtype == 0) {
-    if (D == 128) hipLaunchKernelGGL((token_quant_kernel<BF16, 128>), grid, dim3(256), 0, st, xi, xo, scale_out, rows);
-    else hipLaunchKernelGGL((token_quant_kernel<BF16, 64>), grid, dim3(256), 0, st, xi, xo, scale_out, rows);
+    if (D == 128) hipLaunchKernelGGL((token_quant_kernel<BF16, 128>), grid, dim3(256), 0, st, xi, xo, scale_out, rows, shift);
+    else hipLaunchKernelGGL((token_quant_kernel<BF16, 64>), grid, dim3(256), 0, st, xi, xo, scale_out, rows, shift);
   } else {
-    if (D == 128) hipLaunchKernelGGL((token_quant_kernel<FP16, 128>), grid, dim3(256), 0, st, xi, xo, scale_out, rows);
-    else hipLaunchKernelGGL((token_quant_kernel<FP16, 64>), grid, dim3(256), 0, st, xi, xo, scale_out, rows);
+    if (D == 128) hipLaunchKernelGGL((token_quant_kernel<FP16, 128>), grid, dim3(256), 0, st, xi, xo, scale_out, rows, shift);
+    else hipLaunchKernelGGL((token_quant_kernel<FP16, 64>), grid, dim3(256), 0, st, xi, xo, scale_out, rows, shift);
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ K smoothing
+// k_mean[d] = mean of K over every (batch, head, token) row, rounded to the
+// dtype; two passes in a fixed order (deterministic): block b sums the rows
+// [b*chunk, (b+1)*chunk) (thread t: the 8 channels of 16-byte chunk t % (D/8)
+// over rows t / (D/8) + k * (256 / (D/8)), then the row phases in order), and
+// one block adds the KMEAN_BLOCKS partial sums in block order.
+template <int D, class DT>
+__global__ __launch_bounds__(256) void kmean_partial_kernel(const uint16_t* __restrict__ k, long rows, long chunk,
+                                                            float* __restrict__ part) {
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int RPH = 256 / CPR;      // row phases
+  __shared__ float acc[RPH][D];
+  const int c = threadIdx.x % CPR, ph = threadIdx.x / CPR;
+  const long r0 = (long)blockIdx.x * chunk, r1 = min(rows, r0 + chunk);
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (long r = r0 + ph; r < r1; r += RPH) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(k + r * D + 8 * c);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      s[2 * h] += DT::to_f32((uint16_t)(w[h] & 0xFFFFu));
+      s[2 * h + 1] += DT::to_f32((uint16_t)(w[h] >> 16));
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[ph][8 * c + e] = s[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int d = threadIdx.x;
+    float t = acc[0][d];
+    for (int p = 1; p < RPH; ++p) t += acc[p][d];
+    part[(size_t)blockIdx.x * D + d] = t;
+  }
+}
+
+template <int D, class DT>
+__global__ __launch_bounds__(256) void kmean_final_kernel(const float* __restrict__ part, int nblocks, long rows,
+                                                          float* __restrict__ mean) {
+  const int d = threadIdx.x;
+  if (d >= D) return;
+  float t = 0.0f;
+  for (int b = 0; b < nblocks; ++b) t += part[(size_t)b * D + d];
+  mean[d] = DT::to_f32((uint16_t)DT::pack2(t / (float)rows, 0.0f));
+}
+
+// x - shift[d] rounded to the dtype, 8 elements per thread (D multiple of 8)
+template <int D, class DT>
+__global__ __launch_bounds__(256) void shift_rows_kernel(const uint16_t* __restrict__ x, const float* __restrict__ shift,
+                                                         uint16_t* __restrict__ y, long n8) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const int d0 = (int)((i * 8) % D);
+  const u32x4 w = *reinterpret_cast<const u32x4*>(x + i * 8);
+  u32x4 o;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const float a = DT::to_f32((uint16_t)(w[h] & 0xFFFFu)) - shift[d0 + 2 * h];
+    const float b = DT::to_f32((uint16_t)(w[h] >> 16)) - shift[d0 + 2 * h + 1];
+    o[h] = DT::pack2(a, b);
+  }
+  *reinterpret_cast<u32x4*>(y + i * 8) = o;
+}
+
+template <int D, class DT>
+static void launch_smooth_typed(long rows, const void* k, float* part, float* mean, void* k_smooth, hipStream_t st) {
+  const int nb = (int)min((long)KMEAN_BLOCKS, rows);
+  const long chunk = (rows + nb - 1) / nb;
+  hipLaunchKernelGGL((kmean_partial_kernel<D, DT>), dim3(nb), dim3(256), 0, st, (const uint16_t*)k, rows, chunk, part);
+  hipLaunchKernelGGL((kmean_final_kernel<D, DT>), dim3(1), dim3(256), 0, st, part, nb, rows, mean);
+  if (k_smooth) {
+    const long n8 = rows * D / 8;
+    hipLaunchKernelGGL((shift_rows_kernel<D, DT>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
+                       (const uint16_t*)k, mean, (uint16_t*)k_smooth, n8);
+  }
+}
+
+hipError_t launch_k_smooth(int dtype, int D, long rows, const void* k, float* part, float* mean, void* k_smooth,
+                           hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (dtype == 0) {
+    if (D == 128) launch_smooth_typed<128, BF16>(rows, k, part, mean, k_smooth, st);
+    else launch_smooth_typed<64, BF16>(rows, k, part, mean, k_smooth, st);
+  } else {
+    if (D == 128) launch_smooth_typed<128, FP16>(rows, k, part, mean, k_smooth, st);
+    else launch_smooth_typed<64, FP16>(rows, k, part, mean, k_smooth, st);
   }
   return hipGetLastError();
 }

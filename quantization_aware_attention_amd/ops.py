@@ -23,6 +23,7 @@ QAT_P_QUANT = 1 << 0
 QAT_P_E5M2 = 1 << 1
 QAT_QKV_QUANT = 1 << 2
 QAT_V_FP8_E5M2 = 1 << 3
+QAT_SMOOTH_K = 1 << 4
 QAT_BWD_PREPARE, QAT_BWD_DELTA, QAT_BWD_DQ, QAT_BWD_DKDV = 1, 2, 4, 8
 QAT_BWD_ALL = 15
 

@@ -34,6 +34,7 @@ class Workload:
     v_fp8: bool           # V handed over as e5m2 codes + per-channel scale
     k_offset_var: float   # variance of a per-(head, channel) K offset (0: none)
     seed: int
+    smooth_k: bool = False   # subtract the mean of K over batch, heads, tokens first
 
     @property
     def sm_scale(self) -> float:
@@ -49,6 +50,10 @@ WORKLOADS = {
     "long_video": Workload("long_video", 1, 40, 32768, 32768, 128, "bf16", False, "e4m3", True, False, 0.0, 1003),
     "causal_lm": Workload("causal_lm", 4, 32, 2048, 2048, 128, "bf16", True, "e4m3", False, False, 0.0, 1004),
     "cross_fp8v": Workload("cross_fp8v", 2, 24, 8192, 512, 128, "bf16", False, "e5m2", False, True, 0.0, 1005),
+    # the DiT image shape with per-token Q/K/V quantization of the smoothed K
+    # (its per-channel offsets are what the smoothing takes out before K is quantized)
+    "dit_image_smoothk": Workload("dit_image_smoothk", 1, 24, 4608, 4608, 128, "bf16", False, "e4m3", True, False,
+                                  2.0, 1006, smooth_k=True),
 }
 
 

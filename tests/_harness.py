@@ -28,6 +28,8 @@ def flags_of(w: W.Workload, p_quant=True) -> int:
         f |= ops.QAT_QKV_QUANT
     if w.v_fp8:
         f |= ops.QAT_V_FP8_E5M2
+    if w.smooth_k:
+        f |= ops.QAT_SMOOTH_K
     return f
 
 
@@ -80,7 +82,7 @@ def run_oracle(w: W.Workload, inp: dict, p_quant=True, backward=True, heads=None
     if w.v_fp8:
         v_codes, v_scale = oracle.quantize_v_channels(inp["v"], "e5m2")
     kw = dict(causal=w.causal, p_quant=p_quant, p_fmt=w.p_fmt, qkv_quant=w.qkv_quant,
-              v_codes=v_codes, v_scale=v_scale, heads=heads)
+              v_codes=v_codes, v_scale=v_scale, heads=heads, smooth_k=w.smooth_k, dtype=w.dtype)
     O, O_hp, lse = oracle.attention_forward(inp["q"], inp["k"], inp["v"], w.sm_scale, rows=q_rows, **kw)
     res = {"o": O, "o_hp": O_hp, "lse": lse, "v_codes": v_codes, "v_scale": v_scale}
     if backward:

@@ -100,6 +100,13 @@ def test_workspace_layout():
     qkv = up(6 * 100 * 128 * 2) + 2 * up(6 * 130 * 128 * 2) + up(6 * 100 * 4) + up(6 * 130 * 4)
     assert ops.workspace_bytes(d, ops.QAT_P_QUANT | ops.QAT_QKV_QUANT, 0) == qkv
     assert ops.workspace_bytes(d, ops.QAT_P_QUANT | ops.QAT_QKV_QUANT, 1) == delta + amax + part + qkv
+    # K smoothing (both passes): mean partial sums [256, D] and the mean [D] fp32, and
+    # K - mean (dtype) unless Q/K/V quantization subtracts it on the way
+    sk = up(256 * 128 * 4) + up(128 * 4)
+    ksm = up(6 * 130 * 128 * 2)
+    assert ops.workspace_bytes(d, ops.QAT_SMOOTH_K, 0) == sk + ksm
+    assert ops.workspace_bytes(d, ops.QAT_P_QUANT | ops.QAT_SMOOTH_K, 1) == delta + amax + part + sk + ksm
+    assert ops.workspace_bytes(d, ops.QAT_QKV_QUANT | ops.QAT_SMOOTH_K, 0) == sk + qkv
     big = D(1, 24, 4608, 4608, 128, 0)        # 864 key blocks: capped at 256 partial blocks
     assert ops.workspace_bytes(big, 0, 1) == up(24 * 4608 * 4) + up(256 * 2 * 128 * 128 * 4)
     assert ops.workspace_bytes(d, 0, 2) == 0

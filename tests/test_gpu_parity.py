@@ -15,7 +15,7 @@ import pytest
 import torch
 
 from quantization_aware_attention_amd import workloads as W
-from tests._harness import assert_within, compare, run_gpu, run_oracle
+from tests._harness import assert_within, compare, rel_l2, run_gpu, run_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -38,6 +38,14 @@ SMALL = {
     # 300 key blocks of 128: on 256 compute units, 256 run whole and the last
     # 44 are split over four query ranges whose partials are merged
     "many_heads_tail_split": BASE.with_(B=1, H=300, Nq=128, Nkv=128, seed=24),
+    # K smoothing: plain, before the Q/K/V quantization, fp16 causal D64, fp8 V
+    "smoothk_bf16": BASE.with_(B=1, H=3, Nq=200, Nkv=200, k_offset_var=2.0, smooth_k=True, seed=25),
+    "smoothk_qkv_quant": BASE.with_(B=1, H=2, Nq=190, Nkv=190, qkv_quant=True, k_offset_var=2.0,
+                                    smooth_k=True, seed=26),
+    "smoothk_fp16_causal_d64": BASE.with_(B=2, H=1, Nq=130, Nkv=130, D=64, dtype="fp16", causal=True,
+                                          k_offset_var=1.0, smooth_k=True, seed=27),
+    "smoothk_fp8v": W.WORKLOADS["cross_fp8v"].with_(B=1, H=2, Nq=150, Nkv=500, k_offset_var=1.0,
+                                                     smooth_k=True, seed=28),
 }
 
 
@@ -105,6 +113,7 @@ FULL = {
     "long_video": (W.WORKLOADS["long_video"], [(0, 17)]),
     "causal_lm": (W.WORKLOADS["causal_lm"], [(0, 0), (3, 31)]),
     "cross_fp8v": (W.WORKLOADS["cross_fp8v"], [(0, 5), (1, 23)]),
+    "dit_image_smoothk": (W.WORKLOADS["dit_image_smoothk"], [(0, 0), (0, 23)]),
 }
 
 
@@ -130,3 +139,28 @@ def test_full_size_sampled(name):
     dk = gpu["dk"]
     colsum = np.abs(dk.sum(axis=2)) / (np.abs(dk).sum(axis=2) + 1e-30)
     assert colsum.max() < 2e-2
+
+
+def test_smoothing_equals_plain_on_shifted_keys():
+    """K = K0 + c with every channel of K0 made of +/- pairs on a 1/8 grid and
+    c on a 1/4 grid: the mean over batch, heads and tokens is exactly c in any
+    summation order, and K - c = K0 exactly.  The smoothed run must then be the
+    plain run on K0 bit for bit (O, O_hp, lse, dK, dV).  dQ differs by
+    sm_scale rowsum(dS) c: zero in exact arithmetic, but the kernels take Delta
+    from the dtype-rounded O_hp, which leaves rowsum(dS) at about 1e-3 of its
+    terms; the difference stays inside the dQ parity bar."""
+    w = BASE.with_(B=1, H=2, Nq=160, Nkv=160, k_offset_var=0.0, seed=29)
+    inp = W.make_inputs(w)
+    rng = np.random.default_rng(29)
+    half = rng.integers(-24, 25, size=(w.B, w.H, w.Nkv // 2, w.D)) / 8.0
+    k0 = np.concatenate([half, -half], axis=2)
+    c = rng.integers(-6, 7, size=w.D) / 4.0
+    sh = dict(inp)
+    sh["k"], sh["k_bits"] = W.round_to_dtype(k0 + c, w.dtype)
+    base = dict(inp)
+    base["k"], base["k_bits"] = W.round_to_dtype(k0, w.dtype)
+    smooth = run_gpu(w.with_(smooth_k=True), sh)
+    plain = run_gpu(w, base)
+    for n in ("o", "o_hp", "lse", "dk", "dv"):
+        assert np.array_equal(smooth[n], plain[n]), n
+    assert rel_l2(smooth["dq"], plain["dq"]) < 1e-2
