@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dit_image")
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--kv-chunks", type=int, default=1,
+                    help="chunked-KV mode: the step as C forwards over equal KV chunks (multiples of 64 keys) + "
+                         "qat_attn_merge, and C chunk backwards + qat_attn_sum of the dQ parts")
     ap.add_argument("--cpu-heads", type=int, default=6, help="heads in the oracle sample (0: skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (calibrates HBM byte counters)")
@@ -196,6 +199,36 @@ def main():
         fwd()
         bwd()
 
+    C = args.kv_chunks
+    if C > 1:   # chunked-KV mode (non-causal, plain value inputs): per-chunk buffers outside the timed region
+        if w.causal or w.v_fp8 or w.qkv_quant or w.smooth_k or (w.Nkv // C) % 64 or w.Nkv % C:
+            print("--kv-chunks needs a non-causal workload with plain inputs and Nkv/C a multiple of 64",
+                  file=sys.stderr)
+            sys.exit(2)
+        n = w.Nkv // C
+        kc = [k[:, :, i * n:(i + 1) * n].contiguous() for i in range(C)]
+        vc = [v[:, :, i * n:(i + 1) * n].contiguous() for i in range(C)]
+        outs = [(torch.empty_like(q), torch.empty_like(q), torch.empty_like(lse)) for _ in range(C)]
+        gouts = [(torch.empty_like(q), torch.empty_like(kc[0]), torch.empty_like(vc[0])) for _ in range(C)]
+        cdims = ops.dims_of(q, kc[0])
+        ws_fc = torch.empty(max(256, ops.workspace_bytes(cdims, flags, 0)), device=dev, dtype=torch.uint8)
+        ws_bc = torch.empty(max(256, ops.workspace_bytes(cdims, flags, 1)), device=dev, dtype=torch.uint8)
+
+        def fwd():
+            for i in range(C):
+                ops.attn_fwd(q, kc[i], vc[i], w.sm_scale, False, flags, out=outs[i], workspace=ws_fc)
+            ops.attn_merge([t[0] for t in outs], [t[1] for t in outs], [t[2] for t in outs], out=(o, o_hp, lse))
+
+        def bwd_chunked():
+            for i in range(C):
+                ops.attn_bwd(q, kc[i], vc[i], o_hp, lse, do, w.sm_scale, False, flags, out=gouts[i],
+                             workspace=ws_bc)
+            ops.attn_sum([t[0] for t in gouts], out=dq)
+
+        def step():
+            fwd()
+            bwd_chunked()
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -221,7 +254,8 @@ def main():
         ts = sorted(a.elapsed_time(b) for a, b in evs)
         return {"median": round(ts[len(ts) // 2], 4), "min": round(ts[0], 4)}
 
-    split_ms = {"fwd": per_call(fwd, max(args.steps, 20)), "bwd": per_call(bwd, max(args.steps, 20)),
+    split_ms = {"fwd": per_call(fwd, max(args.steps, 20)),
+                "bwd": per_call(bwd if C == 1 else bwd_chunked, max(args.steps, 20)),
                 "step": per_call(step, max(args.steps, 20))}
 
     Wn = w.B * w.H * w.Nq * w.Nkv * w.D
@@ -330,7 +364,8 @@ def main():
                                f"{', Q/K/V fake-quant e4m3' if w.qkv_quant else ''}"
                                f"{', V e5m2' if w.v_fp8 else ''}",
                    "credited_flop_per_step": credited, "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-                   "fa_convention_tflops": round(fa_conv, 2), "call_ms": split_ms, **extra},
+                   "fa_convention_tflops": round(fa_conv, 2), "call_ms": split_ms,
+                   **({"kv_chunks": C} if C > 1 else {}), **extra},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernel_source_hash": kernel_source_hash(),

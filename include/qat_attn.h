@@ -161,6 +161,31 @@ int qat_attn_bwd_stages(const qat_attn_dims* dims, const void* q, const void* k,
                         void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                         uint32_t stages, void* stream);
 
+/*
+ * Chunked-KV mode on one GPU: the local half of ring attention ("usp:
+ * differentiable operators for training", the ring pass that merges partial
+ * attention by log-sum-exp).  Run qat_attn_fwd on each KV chunk (keys of
+ * chunk c as k, v; non-causal) into (o_c, o_hp_c, lse_c), then
+ *   qat_attn_merge: lse = log sum_c exp(lse_c), o = sum_c exp(lse_c - lse) o_c,
+ *                   o_hp likewise (fp32, chunk order; rounded to the dtype).
+ * With chunk boundaries at multiples of QAT_ATTN_P_GROUP keys this is the
+ * unchunked result up to rounding, the quantized o included (a group's
+ * scale is invariant to the factor exp(lse_c - lse)).  For the backward run
+ * qat_attn_bwd on each chunk with the merged o_hp and lse: its dk, dv are
+ * those of the chunk's keys; the dq of the chunks are added by qat_attn_sum.
+ *  dims: B, H, Nq, D, dtype of the parts (Nkv is not used); n_chunks in
+ *  1..QAT_MERGE_MAX_CHUNKS; *_parts: host arrays of device pointers, each
+ *  part [B,H,Nq,D] (dtype) and lse [B,H,Nq] (fp32), 16-byte aligned.  A row
+ *  whose every lse_c is -inf gives lse = -inf and zero outputs.
+ * qat_attn_sum: out = sum of n_parts tensors [B,H,Nq,D] (dtype), fp32 in part
+ *  order.  Both: QAT_EINVAL for bad dims, counts or pointers; QAT_EHIP.
+ */
+#define QAT_MERGE_MAX_CHUNKS 16
+int qat_attn_merge(const qat_attn_dims* dims, int n_chunks, const void* const* o_parts,
+                   const void* const* o_hp_parts, const float* const* lse_parts,
+                   void* o, void* o_hp, float* lse, void* stream);
+int qat_attn_sum(const qat_attn_dims* dims, int n_parts, const void* const* parts, void* out, void* stream);
+
 /* Workspace bytes needed by the forward (pass 0) or the backward (pass 1);
  * 0 for invalid dims. */
 size_t qat_attn_workspace_bytes(const qat_attn_dims* dims, uint32_t quant_flags, int pass);

@@ -236,11 +236,15 @@ def forward_head(qh, kh, vh, sm_scale, causal=False, p_quant=True, p_fmt="e4m3",
 
 
 def backward_head(qh, kh, vh, do, sm_scale, causal=False, p_quant=True, p_fmt="e4m3",
-                  group=P_GROUP, q_rows=None, k_rows=None, row_block=2048, k_mean=None):
+                  group=P_GROUP, q_rows=None, k_rows=None, row_block=2048, k_mean=None,
+                  lse=None, o_hp=None):
     """Straight-through backward of one head.
 
     ``do`` is dO [Nq, D].  Returns ``(dQ[q_rows], dK[k_rows], dV[k_rows])``
-    (all rows when None).  With ``k_mean`` (K smoothing; ``kh`` is then the
+    (all rows when None).  With ``lse`` and ``o_hp`` (the merged forward of a
+    KV chunk's full row set, chunked mode) P = exp(S - lse) and Delta come
+    from them instead of from this head's own keys.  With ``k_mean`` (K
+    smoothing; ``kh`` is then the
     smoothed K) dQ takes the term sm_scale rowsum(dS) k_mean.  The sums over
     query rows that make dK and dV are
     split into row blocks only to bound memory, and only the columns of P
@@ -262,8 +266,12 @@ def backward_head(qh, kh, vh, do, sm_scale, causal=False, p_quant=True, p_fmt="e
     for b0 in range(0, Nq, row_block):
         r = np.arange(b0, min(Nq, b0 + row_block))
         S = _scores(qh, kh, sm_scale, causal, r)
-        P, _ = _softmax_rows(S)
-        O_hp = P @ vh
+        if lse is None:
+            P, _ = _softmax_rows(S)
+            O_hp = P @ vh
+        else:                                                 # chunk of a longer key set
+            P = np.exp(S - np.asarray(lse, dtype=np.float64)[r][:, None])
+            O_hp = np.asarray(o_hp, dtype=np.float64)[r]
         Delta = np.sum(do[r] * O_hp, axis=1)                  # rowsum(dO o O_hp)
         Ph = np.zeros_like(P)                                 # P^, needed groups only
         for g in groups:
@@ -349,8 +357,11 @@ def attention_forward(q, k, v, sm_scale, causal=False, p_quant=True, p_fmt="e4m3
 
 def attention_backward(q, k, v, do, sm_scale, causal=False, p_quant=True, p_fmt="e4m3",
                        qkv_quant=False, v_codes=None, v_scale=None, group=P_GROUP,
-                       heads=None, q_rows=None, k_rows=None, smooth_k=False, dtype="bf16"):
-    """Straight-through backward over [B, H, N, D]: returns (dQ, dK, dV)."""
+                       heads=None, q_rows=None, k_rows=None, smooth_k=False, dtype="bf16",
+                       lse=None, o_hp=None):
+    """Straight-through backward over [B, H, N, D]: returns (dQ, dK, dV).
+    ``lse`` [B, H, Nq] and ``o_hp`` [B, H, Nq, D] (chunked mode: the merged
+    forward over all chunks) replace this call's own softmax and O_hp."""
     q = np.asarray(q)
     B, H, Nq, D = q.shape
     Nkv = np.asarray(k).shape[2]
@@ -364,8 +375,25 @@ def attention_backward(q, k, v, do, sm_scale, causal=False, p_quant=True, p_fmt=
         qh, kh, vh = _prepare_head(q, k, v, b, h, qkv_quant, v_codes, v_scale, k_mean, dtype)
         dQ[b, h], dK[b, h], dV[b, h] = backward_head(
             qh, kh, vh, np.asarray(do[b, h], dtype=np.float64), sm_scale, causal, p_quant, p_fmt,
-            group, q_rows, k_rows, k_mean=k_mean)
+            group, q_rows, k_rows, k_mean=k_mean,
+            lse=None if lse is None else lse[b, h], o_hp=None if o_hp is None else o_hp[b, h])
     return dQ, dK, dV
+
+
+def merge_chunks(o_parts, o_hp_parts, lse_parts):
+    """Forward results of KV chunks merged by their log-sum-exp:
+    lse = log sum_c exp(lse_c), O = sum_c exp(lse_c - lse) O_c (O_hp alike)."""
+    L = np.stack([np.asarray(x, dtype=np.float64) for x in lse_parts])      # [C, ...rows]
+    m = np.max(L, axis=0)
+    finite = np.isfinite(m)
+    ms = np.where(finite, m, 0.0)
+    w = np.where(np.isfinite(L), np.exp(L - ms), 0.0)
+    tot = np.where(finite, np.sum(w, axis=0), 1.0)                        # >= 1 where finite
+    lse = np.where(finite, ms + np.log(tot), -np.inf)
+    wn = np.where(finite, w / tot, 0.0)                                      # exp(lse_c - lse)
+    O = sum(wn[c][..., None] * np.asarray(o_parts[c], dtype=np.float64) for c in range(len(o_parts)))
+    O_hp = sum(wn[c][..., None] * np.asarray(o_hp_parts[c], dtype=np.float64) for c in range(len(o_parts)))
+    return O, O_hp, lse
 
 
 def flops_fwd_bwd(B, H, Nq, Nkv, D, causal=False):

@@ -235,6 +235,58 @@ int qat_attn_bwd(const qat_attn_dims* dims, const void* q, const void* k, const 
                              dv, workspace, workspace_bytes, QAT_BWD_ALL, stream);
 }
 
+static_assert(QAT_MERGE_MAX_CHUNKS == qat::MERGE_MAX, "merge chunk limit");
+
+static int check_parts_dims(const qat_attn_dims* dims, int n) {
+  if (!dims || n < 1 || n > QAT_MERGE_MAX_CHUNKS) return QAT_EINVAL;
+  const qat_attn_dims& d = *dims;
+  if (d.B < 0 || d.H < 0 || d.Nq < 0 || (d.D != 64 && d.D != 128)) return QAT_EINVAL;
+  if (d.dtype != QAT_DTYPE_BF16 && d.dtype != QAT_DTYPE_FP16) return QAT_EINVAL;
+  return QAT_OK;
+}
+
+int qat_attn_merge(const qat_attn_dims* dims, int n_chunks, const void* const* o_parts,
+                   const void* const* o_hp_parts, const float* const* lse_parts,
+                   void* o, void* o_hp, float* lse, void* stream) {
+  int rc = check_parts_dims(dims, n_chunks);
+  if (rc != QAT_OK) return rc;
+  if (!o_parts || !o_hp_parts || !lse_parts) return QAT_EINVAL;
+  const long rows = (long)dims->B * dims->H * dims->Nq;
+  if (rows == 0) return QAT_OK;
+  qat::MergeArgs a = {};
+  a.n = n_chunks;
+  for (int c = 0; c < n_chunks; ++c) {
+    if (check_ptr(o_parts[c]) || check_ptr(o_hp_parts[c]) || check_ptr(lse_parts[c])) return QAT_EINVAL;
+    a.o[c] = o_parts[c];
+    a.o_hp[c] = o_hp_parts[c];
+    a.lse[c] = lse_parts[c];
+  }
+  if (check_ptr(o) || check_ptr(o_hp) || check_ptr(lse)) return QAT_EINVAL;
+  a.out_o = o;
+  a.out_o_hp = o_hp;
+  a.out_lse = lse;
+  QAT_TRY(qat::launch_merge(dims->dtype, dims->D, rows, a, static_cast<hipStream_t>(stream)));
+  return QAT_OK;
+}
+
+int qat_attn_sum(const qat_attn_dims* dims, int n_parts, const void* const* parts, void* out, void* stream) {
+  int rc = check_parts_dims(dims, n_parts);
+  if (rc != QAT_OK) return rc;
+  if (!parts) return QAT_EINVAL;
+  const long n = (long)dims->B * dims->H * dims->Nq * dims->D;
+  if (n == 0) return QAT_OK;
+  qat::MergeArgs a = {};
+  a.n = n_parts;
+  for (int c = 0; c < n_parts; ++c) {
+    if (check_ptr(parts[c])) return QAT_EINVAL;
+    a.o[c] = parts[c];
+  }
+  if (check_ptr(out)) return QAT_EINVAL;
+  a.out_o = out;
+  QAT_TRY(qat::launch_sum(dims->dtype, n, a, static_cast<hipStream_t>(stream)));
+  return QAT_OK;
+}
+
 int qat_quant_v_fp8(const qat_attn_dims* dims, const void* v, uint8_t* codes, float* v_scale,
                     void* stream) {
   if (!dims) return QAT_EINVAL;

@@ -49,6 +49,22 @@ hipError_t launch_k_smooth(int dtype, int D, long rows, const void* k, float* pa
 hipError_t launch_v_quant(int dtype, int D, int BH, int N, const void* v, uint8_t* codes,
                           float* v_scale, hipStream_t st);
 
+// Chunked-KV merge: up to MERGE_MAX chunks, pointers by value.
+constexpr int MERGE_MAX = 16;
+struct MergeArgs {
+  int n;
+  const void* o[MERGE_MAX];      // merge: O_c; sum: the parts
+  const void* o_hp[MERGE_MAX];
+  const float* lse[MERGE_MAX];
+  void* out_o;
+  void* out_o_hp;
+  float* out_lse;
+};
+// rows = B*H*Nq; tensors [rows, D] (dtype), lse [rows]
+hipError_t launch_merge(int dtype, int D, long rows, const MergeArgs& a, hipStream_t st);
+// out_o[i] = sum_c o[c][i] over n elements (a multiple of 8; dtype)
+hipError_t launch_sum(int dtype, long n, const MergeArgs& a, hipStream_t st);
+
 // FQ test hook on fp32 rows.
 hipError_t launch_fq_rows(const float* x, int rows, int cols, int group, int fmt, uint8_t* codes,
                           float* scales, float* xhat, hipStream_t st);

@@ -78,6 +78,10 @@ def lib():
     L.qat_selftest_exp2_monotone.restype = ctypes.c_int
     L.qat_attn_p_group.argtypes = []
     L.qat_attn_p_group.restype = ctypes.c_int
+    L.qat_attn_merge.argtypes = [dp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]
+    L.qat_attn_merge.restype = ctypes.c_int
+    L.qat_attn_sum.argtypes = [dp, ctypes.c_int, vp, vp, vp]
+    L.qat_attn_sum.restype = ctypes.c_int
     L.qat_attn_strerror.argtypes = [ctypes.c_int]
     L.qat_attn_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -170,6 +174,41 @@ def attn_bwd(q, k, v, o_hp, lse, dout, sm_scale, causal=False, quant_flags=QAT_P
                                    _stream())
     _check("qat_attn_bwd_stages", st)
     return dq, dk, dv
+
+
+QAT_MERGE_MAX_CHUNKS = 16
+
+
+def _ptr_array(ts):
+    return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def attn_merge(o_parts, o_hp_parts, lse_parts, out=None):
+    """Merge the forward results of KV chunks by their log-sum-exp
+    (qat_attn_merge): returns (o, o_hp, lse)."""
+    for i, (o, oh, l) in enumerate(zip(o_parts, o_hp_parts, lse_parts)):
+        _need(o, f"o_parts[{i}]")
+        _need(oh, f"o_hp_parts[{i}]", o_parts[0].dtype)
+        _need(l, f"lse_parts[{i}]", torch.float32)
+    q0 = o_parts[0]
+    o, o_hp, lse = out if out is not None else (torch.empty_like(q0), torch.empty_like(q0),
+                                                torch.empty(q0.shape[:3], dtype=torch.float32, device=q0.device))
+    dims = dims_of(q0, q0)
+    _check("qat_attn_merge", lib().qat_attn_merge(ctypes.byref(dims), len(o_parts), _ptr_array(o_parts),
+                                                  _ptr_array(o_hp_parts), _ptr_array(lse_parts), _ptr(o), _ptr(o_hp),
+                                                  _ptr(lse), _stream()))
+    return o, o_hp, lse
+
+
+def attn_sum(parts, out=None):
+    """Sum of [B, H, N, D] tensors in fp32, part order (qat_attn_sum)."""
+    for i, t in enumerate(parts):
+        _need(t, f"parts[{i}]", parts[0].dtype)
+    out = torch.empty_like(parts[0]) if out is None else out
+    dims = dims_of(parts[0], parts[0])
+    _check("qat_attn_sum", lib().qat_attn_sum(ctypes.byref(dims), len(parts), _ptr_array(parts), _ptr(out),
+                                              _stream()))
+    return out
 
 
 def quant_v_fp8(v):
