@@ -263,7 +263,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) pmax = fmaxf(pmax, p[kb][r]);
     if constexpr (PQ >= 0) {
-      pmax = fmaxf(pmax, shfl_xor32(pmax));
+      pmax = max_xor32(pmax);
       if (g == 0 && qi < Nq) a.p_amax[((size_t)bh * a.NG + t) * Nq + qi] = pmax;
     }
     if constexpr (smooth) {   // K smoothing: sum_j dS_ij (fp32, before any key scale)
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   // others (the keys are masked there).
   // K smoothing: dQ is taken for the original K = (K - k_mean) + k_mean
   float rs = 0.0f;
-  if constexpr (smooth) rs = ds_rowsum + shfl_xor32(ds_rowsum);
+  if constexpr (smooth) rs = sum_xor32(ds_rowsum);
   if (qi >= Nq) return;
   uint16_t* dqp = (uint16_t*)a.dq + (size_t)bh * Nq * D;
 #pragma unroll

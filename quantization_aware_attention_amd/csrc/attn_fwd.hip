@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256, 2) void fwd_f8v_kernel(FwdArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, shfl_xor32(mx));
+      mx = max_xor32(mx);
       const float t_new = mx * c_row;
       const bool resc = t_new > m_used + RESCALE_SLACK;
       if (__any(resc)) {
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(256, 2) void fwd_f8v_kernel(FwdArgs a) {
 
   // ---- epilogue: O = O_acc / l * v_scale[d] (O_hp likewise)
   if (q0 >= Nq) return;
-  const float l = l_part + shfl_xor32(l_part);
+  const float l = sum_xor32(l_part);
   const float inv_l = 1.0f / l;
   uint16_t* op = (uint16_t*)a.o + (size_t)bh * Nq * D;
   uint16_t* ohp = (uint16_t*)a.o_hp + (size_t)bh * Nq * D;
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, shfl_xor32(mx));
+    mx = max_xor32(mx);
     const float t_new = mx * c_row;
     const bool resc = t_new > m_used + RESCALE_SLACK;
     if (__any(resc)) {
@@ -556,7 +556,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 
   // ---- epilogue
   if (qi >= Nq) return;
-  const float l = l_part + shfl_xor32(l_part);
+  const float l = sum_xor32(l_part);
   const float inv_l = 1.0f / l;
   uint16_t* op = (uint16_t*)a.o + (size_t)bh * Nq * D;
   uint16_t* ohp = (uint16_t*)a.o_hp + (size_t)bh * Nq * D;

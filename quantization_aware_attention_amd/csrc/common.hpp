@@ -395,8 +395,23 @@ __device__ __forceinline__ void work_unit(int linear, int total, int nblk, bool 
 }
 
 // ---------------------------------------------------------------- misc
-__device__ __forceinline__ float shfl_xor32(float x) {
-  return __shfl_xor(x, 32, 64);
+// Combine a value with the one held by lane l ^ 32.  v_permlane32_swap
+// exchanges the upper 32 lanes of its first operand with the lower 32 lanes
+// of its second; with x in both, each lane ends up holding its own value in
+// one result and its partner's in the other, so a symmetric combination of
+// the two takes two VALU instructions: no LDS round trip (ds_bpermute, which
+// waits behind the other waves' operand reads) and no lane select.  The two
+// results are read straight from the builtin's return value: copied into a
+// vector first, the second one is lost in code generation.
+__device__ __forceinline__ float max_xor32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
 // v_exp_f32.  The kernels take a row group's P absmax as exp2 of the largest
