@@ -223,6 +223,19 @@ int qat_fake_quant_rows(const float* x, int32_t rows, int32_t cols, int32_t grou
  */
 int qat_selftest_exp2_monotone(float lo, float hi, uint32_t* violations, void* stream);
 
+/*
+ * Self-test of the quantizer's scale pair.  Every kernel computes a group's
+ * s = a / FMAX and r = FMAX / a (correctly rounded fp32 quotients, both 0
+ * when FMAX / a overflows; the quantizer definition above) without the
+ * division instruction sequence: a reciprocal refined by a Newton step and a
+ * remainder correction.  Counts into *mismatches (a device uint32,
+ * overwritten) the positive finite fp32 values a, over all of them, for
+ * which that pair differs in any bit from the one IEEE division gives.
+ * fmt: 0 = e4m3fn (FMAX 448), 1 = e5m2 (FMAX 57344).  Errors: QAT_EINVAL
+ * (null pointer, unknown fmt), QAT_EHIP.
+ */
+int qat_selftest_fq_scale(int32_t fmt, uint32_t* mismatches, void* stream);
+
 /* QAT_ATTN_P_GROUP as compiled into the kernels. */
 int qat_attn_p_group(void);
 

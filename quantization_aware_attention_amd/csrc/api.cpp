@@ -316,6 +316,12 @@ int qat_selftest_exp2_monotone(float lo, float hi, uint32_t* violations, void* s
   return QAT_OK;
 }
 
+int qat_selftest_fq_scale(int32_t fmt, uint32_t* mismatches, void* stream) {
+  if (!mismatches || (fmt != 0 && fmt != 1)) return QAT_EINVAL;
+  QAT_TRY(qat::launch_fq_scale_selftest(fmt, mismatches, static_cast<hipStream_t>(stream)));
+  return QAT_OK;
+}
+
 int qat_attn_p_group(void) { return QAT_ATTN_P_GROUP; }
 
 const char* qat_attn_strerror(int status) {

@@ -483,7 +483,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
     else if (e_kind == 1) d_s[slot][e_q] = ok ? stv : 0.0f;
     else if (e_kind == 2) sq_s[slot][e_q] = ok ? stv : 1.0f;
     else if (PQ >= 0 && e_kind < 3 + NGW) {
-      const FqScale fs = fq_scale(ok ? stv : 0.0f, Fp8Fmt<FQF>::FMAX);
+      const FqScale fs = fq_scale<FQF>(ok ? stv : 0.0f);
       qs_s[slot][e_kind - 3][e_q] = fs.s;
       qr_s[slot][e_kind - 3][e_q] = fs.r;
     }

@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256, 2) void fwd_f8v_kernel(FwdArgs a) {
       FqScale fs = {0.0f, 0.0f};
       if constexpr (PQ >= 0) {
         const float pmax = (mx == -INFINITY) ? 0.0f : fast_exp2(__builtin_fmaf(mx, c_row, -m_sub));
-        fs = fq_scale(pmax, Fp8Fmt<FQF>::FMAX);
+        fs = fq_scale<FQF>(pmax);
       }
       // ---- p = exp2(S*c - m); operands: P^ codes (dword 4kb + u = keys
       // 32kb + 8u + 4g + 0..3) and P_hp in fp16 (k step kk = 2kb + h)
@@ -470,7 +470,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     FqScale fs = {0.0f, 0.0f};
     if constexpr (PQ >= 0) {   // absmax of the row group = exp2 of its largest argument
       const float pmax = (mx == -INFINITY) ? 0.0f : fast_exp2(__builtin_fmaf(mx, c_row, -m_sub));
-      fs = fq_scale(pmax, Fp8Fmt<FQF>::FMAX);
+      fs = fq_scale<FQF>(pmax);
     }
     const FqScale f4[4] = {fs, fs, fs, fs};
     float psum = 0.0f;

@@ -165,20 +165,7 @@ struct TileCopy {
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
 // ---------------------------------------------------------------- FQ
-// One group's scale pair: s = fp32(a/FMAX), r = fp32(FMAX/a), both correctly
-// rounded divisions; a == 0 or an r that overflows gives s = r = 0 (the group
-// quantizes to zeros).
 struct FqScale { float s, r; };
-
-__device__ __forceinline__ FqScale fq_scale(float a, float fmax) {
-  float r = fmax / a;
-  float s = a / fmax;
-  const bool ok = (a > 0.0f) && (r <= 3.402823466e38f);
-  FqScale q;
-  q.s = ok ? s : 0.0f;
-  q.r = ok ? r : 0.0f;
-  return q;
-}
 
 // FMT: 0 = e4m3fn (FMAX 448), 1 = e5m2 (FMAX 57344)
 template <int FMT> struct Fp8Fmt;
@@ -200,6 +187,39 @@ template <> struct Fp8Fmt<1> {
     return __builtin_amdgcn_cvt_pk_f32_bf8((int)pk, false);
   }
 };
+
+// One group's scale pair from its absmax a: s = a/FMAX and r = FMAX/a, each
+// the correctly rounded fp32 quotient; a == 0 or an r that overflows gives
+// s = r = 0 (the group quantizes to zeros).  Computed without the division
+// sequence (a dependent chain of about a dozen instructions per quotient):
+//  * s: s0 = a*z with z = RN(1/FMAX); the remainder a - s0*FMAX is exact in
+//    one fma, and s0 + remainder*z rounds to the correctly rounded quotient;
+//  * r: the hardware reciprocal of a refined by one Newton step (y1), then
+//    q = FMAX*y1 corrected by its exact remainder FMAX - a*q (Markstein's
+//    correction).  From a = 2^64 up, a and FMAX are both scaled by 2^-32
+//    first (exact), which keeps 1/a out of the subnormal range.
+// Both FMAX values are 1.75 * 2^k.  For every positive finite fp32 a, s, r
+// and the flush decision equal those of the two IEEE divisions: checked
+// exhaustively, for both formats, by qat_selftest_fq_scale.
+template <int FMT>
+__device__ __forceinline__ FqScale fq_scale(float a) {
+  constexpr float F = Fp8Fmt<FMT>::FMAX;
+  constexpr float z = 1.0f / F;
+  const float s0 = a * z;
+  const float s = __builtin_fmaf(__builtin_fmaf(-s0, F, a), z, s0);
+  const bool big = a >= 0x1p64f;
+  const float as = big ? a * 0x1p-32f : a;
+  const float fs = big ? F * 0x1p-32f : F;
+  const float y = __builtin_amdgcn_rcpf(as);
+  const float y1 = __builtin_fmaf(__builtin_fmaf(-as, y, 1.0f), y, y);
+  const float q = fs * y1;
+  const float r = __builtin_fmaf(__builtin_fmaf(-as, q, fs), y1, q);
+  const bool ok = (a > 0.0f) && (r <= 3.402823466e38f);
+  FqScale out;
+  out.s = ok ? s : 0.0f;
+  out.r = ok ? r : 0.0f;
+  return out;
+}
 
 // Fake-quantize a pair of values: v = fp32(x*r), code = RNE(v), x^ = fp32(code*s).
 // The two values may belong to different groups (scales q0, q1).  Returns

@@ -71,6 +71,7 @@ hipError_t launch_fq_rows(const float* x, int rows, int cols, int group, int fmt
 
 // Self-test: count decreasing adjacent pairs of v_exp_f32 over fp32 [lo, hi].
 hipError_t launch_exp2_selftest(float lo, float hi, uint32_t* violations, hipStream_t st);
+hipError_t launch_fq_scale_selftest(int fmt, uint32_t* mismatches, hipStream_t st);
 
 // Backward pieces.
 hipError_t launch_bwd_delta(const Shape& s, const void* o_hp, const void* dout, float* delta,

@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void token_quant_kernel(const uint16_t* __rest
   for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(v[e]));
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
-  const FqScale fs = fq_scale(amax, Fp8Fmt<0>::FMAX);
+  const FqScale fs = fq_scale<0>(amax);
   const bool split = scale_out != nullptr;
   const FqScale unit = {1.0f, fs.r};   // code value times 1: the code itself
   uint32_t outw[EPL / 2];
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict
     float m = part[0][d];
 #pragma unroll
     for (int p = 1; p < RPS; ++p) m = fmaxf(m, part[p][d]);
-    const FqScale fs = fq_scale(m, Fp8Fmt<1>::FMAX);
+    const FqScale fs = fq_scale<1>(m);
     scale_s[d] = fs.s;
     scale_r[d] = fs.r;
     v_scale[(size_t)bh * D + d] = fs.s;
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(256) void fq_rows_kernel(const float* __restrict__ 
   const float* src = x + (size_t)row * cols;
   float amax = 0.0f;
   for (int c = c0; c < c1; ++c) amax = fmaxf(amax, fabsf(src[c]));
-  const FqScale fs = fq_scale(amax, Fp8Fmt<FMT>::FMAX);
+  const FqScale fs = fq_scale<FMT>(amax);
   if (scales) scales[(size_t)row * ng + gi] = fs.s;
   const bool zero = fs.r == 0.0f;
   for (int c = c0; c < c1; c += 2) {
@@ -283,6 +283,31 @@ __global__ __launch_bounds__(256) void exp2_monotone_kernel(uint32_t key_lo, uin
 
 __global__ void zero_u32(uint32_t* p) { *p = 0; }
 
+// Self-test: count the positive finite fp32 values a whose fq_scale pair
+// differs in any bit from (a/FMAX, FMAX/a) by IEEE division, or from (0, 0)
+// where FMAX/a overflows.  Each thread walks one contiguous run of bit
+// patterns of [1, 0x7F7FFFFF].
+constexpr uint32_t FQS_LAST = 0x7F7FFFFFu;   // largest finite fp32
+constexpr uint32_t FQS_PER_THREAD = 4096;
+
+template <int FMT>
+__global__ __launch_bounds__(256) void fq_scale_selftest_kernel(uint32_t* mismatches) {
+  const uint64_t start = 1 + ((uint64_t)blockIdx.x * 256 + threadIdx.x) * FQS_PER_THREAD;
+  if (start > FQS_LAST) return;
+  const uint64_t stop = min((uint64_t)FQS_LAST, start + FQS_PER_THREAD - 1);
+  constexpr float F = Fp8Fmt<FMT>::FMAX;
+  uint32_t bad = 0;
+  for (uint64_t u = start; u <= stop; ++u) {
+    const float a = __builtin_bit_cast(float, (uint32_t)u);
+    const float r_ref = F / a, s_ref = a / F;
+    const bool ok = r_ref <= 3.402823466e38f;
+    const FqScale q = fq_scale<FMT>(a);
+    bad += (__builtin_bit_cast(uint32_t, q.s) != __builtin_bit_cast(uint32_t, ok ? s_ref : 0.0f)) ||
+           (__builtin_bit_cast(uint32_t, q.r) != __builtin_bit_cast(uint32_t, ok ? r_ref : 0.0f));
+  }
+  if (bad) atomicAdd(mismatches, bad);
+}
+
 hipError_t launch_exp2_selftest(float lo, float hi, uint32_t* violations, hipStream_t st) {
   auto key = [](float f) {
     const uint32_t b = __builtin_bit_cast(uint32_t, f);
@@ -295,6 +320,15 @@ hipError_t launch_exp2_selftest(float lo, float hi, uint32_t* violations, hipStr
   const uint64_t threads = ((uint64_t)khi - klo + per - 1) / per;
   hipLaunchKernelGGL(exp2_monotone_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, klo, khi, per,
                      violations);
+  return hipGetLastError();
+}
+
+hipError_t launch_fq_scale_selftest(int fmt, uint32_t* mismatches, hipStream_t st) {
+  hipLaunchKernelGGL(zero_u32, dim3(1), dim3(1), 0, st, mismatches);
+  const uint64_t threads = (FQS_LAST + (uint64_t)FQS_PER_THREAD - 1) / FQS_PER_THREAD;
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (fmt == 0) hipLaunchKernelGGL(fq_scale_selftest_kernel<0>, grid, dim3(256), 0, st, mismatches);
+  else hipLaunchKernelGGL(fq_scale_selftest_kernel<1>, grid, dim3(256), 0, st, mismatches);
   return hipGetLastError();
 }
 

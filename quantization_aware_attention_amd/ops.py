@@ -76,6 +76,8 @@ def lib():
     L.qat_fake_quant_rows.restype = ctypes.c_int
     L.qat_selftest_exp2_monotone.argtypes = [f32, f32, vp, vp]
     L.qat_selftest_exp2_monotone.restype = ctypes.c_int
+    L.qat_selftest_fq_scale.argtypes = [i32, vp, vp]
+    L.qat_selftest_fq_scale.restype = ctypes.c_int
     L.qat_attn_p_group.argtypes = []
     L.qat_attn_p_group.restype = ctypes.c_int
     L.qat_attn_merge.argtypes = [dp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]
@@ -233,6 +235,15 @@ def fake_quant_rows(x, group, fmt):
     _check("qat_fake_quant_rows", lib().qat_fake_quant_rows(_ptr(x), rows, cols, group, fmt, _ptr(codes),
                                                             _ptr(scales), _ptr(xhat), _stream()))
     return codes, scales, xhat
+
+
+def selftest_fq_scale(fmt: int) -> int:
+    """Number of positive finite fp32 absmax values whose quantizer scale pair
+    (s, r) on the GPU differs from the IEEE quotients (fmt 0: e4m3, 1: e5m2)."""
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    _check("qat_selftest_fq_scale", lib().qat_selftest_fq_scale(int(fmt), _ptr(out), _stream()))
+    torch.cuda.synchronize()
+    return int(out.item())
 
 
 def selftest_exp2_monotone(lo=float("-inf"), hi=128.0) -> int:

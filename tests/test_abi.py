@@ -123,3 +123,6 @@ def test_other_entry_points_validate(L):
     assert L.qat_selftest_exp2_monotone(0.0, 1.0, None, None) == ops.QAT_EINVAL
     assert L.qat_selftest_exp2_monotone(2.0, 1.0, FAKE, None) == ops.QAT_EINVAL
     assert L.qat_selftest_exp2_monotone(float("nan"), 1.0, FAKE, None) == ops.QAT_EINVAL
+    assert L.qat_selftest_fq_scale(0, None, None) == ops.QAT_EINVAL
+    assert L.qat_selftest_fq_scale(2, FAKE, None) == ops.QAT_EINVAL
+    assert L.qat_selftest_fq_scale(-1, FAKE, None) == ops.QAT_EINVAL

@@ -135,3 +135,14 @@ def test_exp2_is_monotone_over_all_fp32():
     # never decreases.  Checked over every fp32 value from -inf to 128.
     from quantization_aware_attention_amd import ops
     assert ops.selftest_exp2_monotone(float("-inf"), 128.0) == 0
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_fq_scale_equals_ieee_division_over_all_fp32(fmt):
+    # The kernels form a group's s = a/FMAX and r = FMAX/a without the
+    # division sequence (reciprocal, Newton step, remainder correction).
+    # Every positive finite fp32 a must give the IEEE quotients bit for bit,
+    # and (0, 0) exactly where FMAX/a overflows.
+    from quantization_aware_attention_amd import ops
+    print(f"fq_scale self-test, fmt {fmt}", flush=True)
+    assert ops.selftest_fq_scale(fmt) == 0
