@@ -358,7 +358,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
   constexpr int NST = NST2 + 2 * NKS;       // + S/dP MFMAs
   constexpr int NGRP = 8;                   // fenced groups per iteration
   constexpr int GSZ = NST / NGRP;           // MFMAs per group
-  constexpr int AHEAD = 2;                  // MFMA steps whose LDS operand is in flight
+  constexpr int AHEAD = 4;                  // MFMA steps whose LDS operand is in flight
   static_assert(NST % NGRP == 0 && NCH >= 1, "shape");
   __shared__ __attribute__((aligned(16))) char q_s[DSP_SLOTS][TILE];
   __shared__ __attribute__((aligned(16))) char do_s[DSP_SLOTS][TILE];
