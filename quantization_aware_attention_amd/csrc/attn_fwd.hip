@@ -551,7 +551,13 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       mfma_phase(t_work);
       prio_valu();
     }
-    if (ph_i + 1 < nphase) __syncthreads();
+    // Barriers: after every odd phase (group 0's VALU phase), which publishes
+    // the tiles it copied and orders those copies after the last reads of the
+    // buffers they overwrite (made in the odd phase two earlier).  The plain
+    // VALU phase reads no LDS, so even phases need none.  With per-token codes
+    // they do: group 0's odd phase rewrites the key-scale buffer that group
+    // 1's VALU phase reads in the even phase before it.
+    if (ph_i + 1 < nphase && (QKS || (ph_i & 1))) __syncthreads();
   }
 
   // ---- epilogue
