@@ -96,14 +96,26 @@ __global__ __launch_bounds__(256) void kmean_partial_kernel(const uint16_t* __re
   const int c = threadIdx.x % CPR, ph = threadIdx.x / CPR;
   const long r0 = (long)blockIdx.x * chunk, r1 = min(rows, r0 + chunk);
   float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (long r = r0 + ph; r < r1; r += RPH) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(k + r * D + 8 * c);
+  auto add = [&](const u32x4& w) {
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       s[2 * h] += DT::to_f32((uint16_t)(w[h] & 0xFFFFu));
       s[2 * h + 1] += DT::to_f32((uint16_t)(w[h] >> 16));
     }
+  };
+  // eight rows' loads in flight per thread (one at a time leaves the chip far
+  // below HBM bandwidth); the additions keep the row order, so the sums do
+  // not depend on the unrolling
+  constexpr int UNR = 8;
+  long r = r0 + ph;
+  for (; r + (UNR - 1) * RPH < r1; r += UNR * RPH) {
+    u32x4 w[UNR];
+#pragma unroll
+    for (int i = 0; i < UNR; ++i) w[i] = *reinterpret_cast<const u32x4*>(k + (r + i * RPH) * D + 8 * c);
+#pragma unroll
+    for (int i = 0; i < UNR; ++i) add(w[i]);
   }
+  for (; r < r1; r += RPH) add(*reinterpret_cast<const u32x4*>(k + r * D + 8 * c));
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[ph][8 * c + e] = s[e];
   __syncthreads();
@@ -120,8 +132,18 @@ __global__ __launch_bounds__(256) void kmean_final_kernel(const float* __restric
                                                           float* __restrict__ mean) {
   const int d = threadIdx.x;
   if (d >= D) return;
+  // sixteen partials' loads in flight, added in block order
+  constexpr int UNR = 16;
   float t = 0.0f;
-  for (int b = 0; b < nblocks; ++b) t += part[(size_t)b * D + d];
+  int b = 0;
+  for (; b + UNR <= nblocks; b += UNR) {
+    float v[UNR];
+#pragma unroll
+    for (int i = 0; i < UNR; ++i) v[i] = part[(size_t)(b + i) * D + d];
+#pragma unroll
+    for (int i = 0; i < UNR; ++i) t += v[i];
+  }
+  for (; b < nblocks; ++b) t += part[(size_t)b * D + d];
   mean[d] = DT::to_f32((uint16_t)DT::pack2(t / (float)rows, 0.0f));
 }
 
