@@ -304,10 +304,12 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   constexpr int NKS = D / 16;
   constexpr int FQF = PQ >= 0 ? PQ : 0;
   constexpr int NPV = 4 * NDB;   // P@V steps of an MFMA phase
-  constexpr int PP_AHEAD = 6;   // fragments in flight ahead of their MFMAs
+  // fragments in flight ahead of their MFMAs (per-token codes: fewer, whose
+  // registers keep that variant free of most spills)
+  constexpr int PP_AHEAD = QKS ? 4 : 6;
   __shared__ __attribute__((aligned(16))) char kbuf[2][TILE];
   __shared__ __attribute__((aligned(16))) char vbuf[2][TILE];
-  __shared__ __attribute__((aligned(16))) float ks_s[2][FWD_BN];   // IN_QKS: key scales of K(t)
+  __shared__ __attribute__((aligned(16))) float ks_s[3][FWD_BN];   // IN_QKS: key scales of K(t)
   __shared__ __attribute__((aligned(16))) char qbuf[PP_BM * D * 2];   // the block's Q rows
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const f32x4 sk = *reinterpret_cast<const f32x4*>(&ks_s[t & 1][kb * 32 + 8 * u + 4 * g]);
+          const f32x4 sk = *reinterpret_cast<const f32x4*>(&ks_s[t % 3][kb * 32 + 8 * u + 4 * g]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) s[kb][4 * u + e] *= sk[e];
         }
@@ -433,9 +435,10 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   };
   auto valu_phase = [&](int t) __attribute__((always_inline)) {
     if (!active(t)) return;
-    // IN_QKS: the key scales of tile t stay in ks_s[t & 1] until group 0's
-    // VALU phase of tile t + 1 rewrites that buffer, after both groups' VALU
-    // phases of tile t
+    // IN_QKS: the key scales of tile t are in ks_s[t % 3], written at the end
+    // of group 0's copy phase 2t - 1 and read in phases 2t + 1 (group 0) and
+    // 2t + 2 (group 1); the buffer is next rewritten at the end of phase
+    // 2t + 5, after the barrier that follows phase 2t + 3
     scale_keys(t);
     const int kv0 = t * FWD_BN;
     if ((kv0 + FWD_BN > Nkv) || (CAUSAL && kv0 + FWD_BN - 1 > q0)) {
@@ -544,20 +547,20 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     wait_vmem();
     if constexpr (QKS) {
       const int t = ph_i >> 1;
-      if (grp == 0 && !mfma_now && t + 1 < T && tid < FWD_BN) ks_s[(t + 1) & 1][tid] = ksreg;
+      if (grp == 0 && !mfma_now && t + 1 < T && tid < FWD_BN) ks_s[(t + 1) % 3][tid] = ksreg;
     }
     if (mfma_now) {   // raised issue priority: the MFMAs go first, the other wave's VALU work fills in
       prio_mfma();
       mfma_phase(t_work);
       prio_valu();
     }
-    // Barriers: after every odd phase (group 0's VALU phase), which publishes
-    // the tiles it copied and orders those copies after the last reads of the
-    // buffers they overwrite (made in the odd phase two earlier).  The plain
-    // VALU phase reads no LDS, so even phases need none.  With per-token codes
-    // they do: group 0's odd phase rewrites the key-scale buffer that group
-    // 1's VALU phase reads in the even phase before it.
-    if (ph_i + 1 < nphase && (QKS || (ph_i & 1))) __syncthreads();
+    // Barriers: after every odd phase (group 0's VALU phase) only.  That
+    // barrier publishes the tiles (and key scales) group 0 copied in the
+    // phase, and orders each copy after the last reads of the buffer it
+    // overwrites: K/V buffers were last read in the odd phase two earlier,
+    // and the three key-scale buffers in the phases before that (the VALU
+    // phases read no other LDS), so even phases need no barrier.
+    if (ph_i + 1 < nphase && (ph_i & 1)) __syncthreads();
   }
 
   // ---- epilogue
