@@ -173,6 +173,13 @@ int qat_attn_bwd_stages(const qat_attn_dims* dims, const void* q, const void* k,
  * scale is invariant to the factor exp(lse_c - lse)).  For the backward run
  * qat_attn_bwd on each chunk with the merged o_hp and lse: its dk, dv are
  * those of the chunk's keys; the dq of the chunks are added by qat_attn_sum.
+ * Flags: per-token Q/K/V quantization is per row, so chunking leaves it
+ * unchanged; with fp8 V pass each chunk's codes with the unchunked v_scale.
+ * QAT_SMOOTH_K does not carry over: each chunk would be smoothed by the mean
+ * of its own keys, which shifts its lse_c by a different per-row constant
+ * and so breaks the merge weights.  Subtract one mean over all keys from K
+ * before chunking instead (softmax does not change; dQ then lacks the
+ * rowsum(dS) * k_mean term, which the caller adds).
  *  dims: B, H, Nq, D, dtype of the parts (Nkv is not used); n_chunks in
  *  1..QAT_MERGE_MAX_CHUNKS; *_parts: host arrays of device pointers, each
  *  part [B,H,Nq,D] (dtype) and lse [B,H,Nq] (fp32), 16-byte aligned.  A row
