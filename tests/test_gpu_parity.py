@@ -35,6 +35,11 @@ SMALL = {
     "one_query": BASE.with_(B=1, H=2, Nq=1, Nkv=200, seed=20),
     "causal_one": BASE.with_(B=1, H=1, Nq=1, Nkv=1, causal=True, seed=21),
     "tile_aligned": BASE.with_(B=1, H=1, Nq=256, Nkv=128, seed=22),
+    # per-token codes over many key tiles (the forward's key-scale buffers are
+    # reused), in both kernels' other variants
+    "bf16_qkv_quant_long_cross": BASE.with_(B=1, H=2, Nq=150, Nkv=900, qkv_quant=True, seed=31),
+    "fp16_qkv_quant_causal_d64": BASE.with_(B=1, H=2, Nq=400, Nkv=400, D=64, dtype="fp16", causal=True,
+                                            qkv_quant=True, seed=32),
     # 300 key blocks of 128: on 256 compute units, 256 run whole and the last
     # 44 are split over four query ranges whose partials are merged
     "many_heads_tail_split": BASE.with_(B=1, H=300, Nq=128, Nkv=128, seed=24),
