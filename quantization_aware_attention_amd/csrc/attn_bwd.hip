@@ -115,10 +115,12 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   constexpr int TILE = DQ_BN * D * 2;
   constexpr int NDB = D / 32;
   constexpr int NKS = D / 16;
-  constexpr int CH = D / 8;
-  constexpr int LPT = DQ_BN * CH / 256;
   __shared__ __attribute__((aligned(16))) char smem[2][2][TILE];   // [buffer][K, V]
   __shared__ __attribute__((aligned(16))) float ks_s[2][DQ_BN];     // IN_QKS: key scales
+  // IN_VFP8: the next tile's V codes, copied HBM -> LDS by DMA
+  constexpr int VC_BYTES = VFP8 ? DQ_BN * D : 16;
+  constexpr int VC_PER_THREAD = DQ_BN * D / (256 * 16);   // 16-byte chunks per thread
+  __shared__ __attribute__((aligned(16))) char vc_s[VC_BYTES];
 
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int ntq = (a.Nq + DQ_BM - 1) / DQ_BM;
@@ -141,6 +143,18 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
     const bool ok = qi < Nq;
     qf[ks] = ok ? *reinterpret_cast<const s16x8*>(qp + (size_t)qi * D + 16 * ks + 8 * g) : (s16x8){};
     dof[ks] = ok ? *reinterpret_cast<const s16x8*>(dop + (size_t)qi * D + 16 * ks + 8 * g) : (s16x8){};
+    if constexpr (VFP8) {   // dP = (dO * v_scale) code^T: the per-channel V scale moves onto dO
+      const f32x4 s0 = *reinterpret_cast<const f32x4*>(vsc + 16 * ks + 8 * g);
+      const f32x4 s1 = *reinterpret_cast<const f32x4*>(vsc + 16 * ks + 8 * g + 4);
+      const float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+      const u32x4 wd = __builtin_bit_cast(u32x4, dof[ks]);
+      u32x4 ws;
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        ws[h] = BF16::pack2(BF16::to_f32((uint16_t)(wd[h] & 0xFFFFu)) * sc[2 * h],
+                            BF16::to_f32((uint16_t)(wd[h] >> 16)) * sc[2 * h + 1]);
+      dof[ks] = __builtin_bit_cast(s16x8, ws);
+    }
   }
   const float Mi = qi < Nq ? a.lse[(size_t)bh * Nq + qi] * LOG2E : 0.0f;
   const float Di = qi < Nq ? a.delta[(size_t)bh * Nq + qi] : 0.0f;
@@ -155,9 +169,12 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   constexpr bool smooth = SMK;
   float ds_rowsum = 0.0f;   // this lane's half of sum_j dS_ij (K smoothing)
 
-  // K tiles (and V, unless fp8) go HBM -> LDS directly, double-buffered; fp8
-  // V codes and key scales take a register detour.
-  u32x2 vcode[LPT];
+  // K tiles (and V, unless fp8) go HBM -> LDS directly, double-buffered.  fp8
+  // V codes go HBM -> LDS by DMA too, into one 8-bit tile in plain row order:
+  // chunk u of a thread is the 16 bytes at P = (4u + wave) KiB + 16 lane,
+  // and the same thread decodes exactly those bytes after its own copies
+  // completed, so the decode needs no barrier.  Key scales take a register
+  // detour.
   float ksreg = 0.0f;
   TileCopy<D, DQ_BN, 4> copy;
   copy.init(w, lane);
@@ -165,10 +182,11 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
     copy.issue(smem[buf][0], kp, t * DQ_BN, Nkv);
     if constexpr (VFP8) {
 #pragma unroll
-      for (int u = 0; u < LPT; ++u) {
-        const int idx = tid + 256 * u, row = idx / CH, ch = idx % CH;
-        const int key = min(t * DQ_BN + row, Nkv - 1);
-        vcode[u] = *reinterpret_cast<const u32x2*>(vp + (size_t)key * D + ch * 8);
+      for (int u = 0; u < VC_PER_THREAD; ++u) {
+        const int blk = u * 4 + w, P = blk * 1024 + lane * 16;
+        const int key = min(t * DQ_BN + P / D, Nkv - 1);   // tail rows repeat the last key (masked)
+        __builtin_amdgcn_global_load_lds((const void*)(vp + (size_t)key * D + P % D),
+                                         (lds_void*)(vc_s + blk * 1024), 16, 0, 0);
       }
     } else {
       copy.issue(smem[buf][1], (const uint16_t*)vp, t * DQ_BN, Nkv);
@@ -179,20 +197,21 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
     }
   };
   auto finish_tile = [&](int buf) {
-    if constexpr (VFP8) {   // V^ = code * v_scale[d], rounded to bf16
+    if constexpr (VFP8) {   // the code values themselves (exact in bf16); v_scale is on dO
 #pragma unroll
-      for (int u = 0; u < LPT; ++u) {
-        const int idx = tid + 256 * u, row = idx / CH, ch = idx % CH;
-        const f32x4 s0 = *reinterpret_cast<const f32x4*>(vsc + ch * 8);
-        const f32x4 s1 = *reinterpret_cast<const f32x4*>(vsc + ch * 8 + 4);
-        const float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-        u32x4 vv;
+      for (int u = 0; u < VC_PER_THREAD; ++u) {
+        const int P = (u * 4 + w) * 1024 + lane * 16, row = P / D, c0 = P % D;
+        const u32x4 codes = *reinterpret_cast<const u32x4*>(vc_s + P);
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const f32x2 f = __builtin_amdgcn_cvt_pk_f32_bf8((int)(vcode[u][h >> 1] >> (16 * (h & 1))), false);
-          vv[h] = BF16::pack2(f[0] * sc[2 * h], f[1] * sc[2 * h + 1]);
+        for (int h2 = 0; h2 < 2; ++h2) {   // 8 codes -> one 16-byte chunk of the bf16 tile
+          u32x4 vv;
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const f32x2 f = __builtin_amdgcn_cvt_pk_f32_bf8((int)(codes[2 * h2 + (h >> 1)] >> (16 * (h & 1))), false);
+            vv[h] = BF16::pack2(f[0], f[1]);
+          }
+          *reinterpret_cast<u32x4*>(smem[buf][1] + tile_off<D>(row, c0 / 8 + h2)) = vv;
         }
-        *reinterpret_cast<u32x4*>(smem[buf][1] + tile_off<D>(row, ch)) = vv;
       }
     }
     if constexpr (QKS) {
