@@ -359,11 +359,19 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 
   auto scale_keys = [&](int t) __attribute__((always_inline)) {   // IN_QKS: S^T *= per-key scales
     if constexpr (QKS) {
+      // the lane's half (g) recomputed here from the lane counter: held from
+      // the kernel's start, its address was spilled, and the reload's vmcnt
+      // wait also waited for the tile copies just issued
+      // (an opaque all-ones mask keeps the count from being hoisted out of
+      // the loop and spilled in turn)
+      uint32_t ones = ~0u;
+      asm volatile("" : "+s"(ones));
+      const int gh = (int)__builtin_amdgcn_mbcnt_hi(ones, __builtin_amdgcn_mbcnt_lo(ones, 0u)) >> 5;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const f32x4 sk = *reinterpret_cast<const f32x4*>(&ks_s[t % 3][kb * 32 + 8 * u + 4 * g]);
+          const f32x4 sk = *reinterpret_cast<const f32x4*>(&ks_s[t % 3][kb * 32 + 8 * u + 4 * gh]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) s[kb][4 * u + e] *= sk[e];
         }
