@@ -356,11 +356,14 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 //                    packed as the next iteration's operands,
 // in eight fenced groups of MFMAs plus a slice of the vector work, so the
 // matrix core runs under the vector work of the same wave.  Q/dO blocks are
-// staged through registers: loaded from HBM in iteration b-3, written to LDS
-// slot b%4 in iteration b-2, read in iterations b-1 .. b+1.
+// staged through registers: loaded from HBM in iteration b-4, written to LDS
+// slot b%8 in iteration b-3, read in iterations b-1 .. b+1.  A barrier ends
+// every odd iteration only: a block written in iteration c is first read in
+// c + 2, after the barrier that ends c or c + 1, and the block its slot held
+// before was last read in c - 4, two barriers earlier.
 constexpr int DSP_BN = 128;    // keys per workgroup
 constexpr int DSP_BQ = 32;     // queries per block
-constexpr int DSP_SLOTS = 4;   // LDS block slots
+constexpr int DSP_SLOTS = 8;   // LDS block slots
 
 template <class DT, int D, bool CAUSAL, int PQ, int IN>
 __global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
@@ -625,20 +628,21 @@ __global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
   // iteration b: S, DP = block b (in), S2, DP2 = block b+1 (out);
   // Pp, DSp = operands of block b-1 (in), Pn, DSn = operands of block b (out)
   auto iteration = [&](int b, f32x16& S, f32x16& DP, f32x16& S2, f32x16& DP2, const uint32_t (&Pp)[8],
-                       const uint32_t (&DSp)[8], uint32_t (&Pn)[8], uint32_t (&DSn)[8]) __attribute__((always_inline)) {
+                       const uint32_t (&DSp)[8], uint32_t (&Pn)[8], uint32_t (&DSn)[8],
+                       bool sync) __attribute__((always_inline)) {
     const bool do2 = b >= 1 && active(b - 1);
     const bool do1 = b + 1 < NB && active(b + 1);
     const bool dov = b < NB && active(b);
     const bool full = do2 && do1 && dov;
-    // staging of block b+2 (loaded in iteration b-1) and loads of block b+3:
+    // staging of block b+3 (loaded in iteration b-1) and loads of block b+4:
     // inside the first fenced groups on the full path, up front otherwise
-    const bool stw = b + 2 < NB, stl = b + 3 < NB;
+    const bool stw = b + 3 < NB, stl = b + 4 < NB;
     if (!full) {
       if (stw) {
-        write_tiles(b + 2);
-        write_vec(b + 2);
+        write_tiles(b + 3);
+        write_vec(b + 3);
       }
-      if (stl) load_stage(b + 3);
+      if (stl) load_stage(b + 4);
     }
     if (dov) {   // masked scores -> -inf before the exponent
       const int q0 = qstart(b);
@@ -665,9 +669,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
           step(cur, st, Pp, DSp, S2, DP2);
         }
         valu_piece(j, b, S, DP, Pn, DSn);
-        if (j == 0 && stw) write_tiles(b + 2);
-        if (j == 1 && stw) write_vec(b + 2);
-        if (j == 2 && stl) load_stage(b + 3);
+        if (j == 0 && stw) write_tiles(b + 3);
+        if (j == 1 && stw) write_vec(b + 3);
+        if (j == 2 && stl) load_stage(b + 4);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
@@ -684,29 +688,27 @@ __global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
         for (int j = 0; j < NGRP; ++j) valu_piece(j, b, S, DP, Pn, DSn);
       }
     }
-    __syncthreads();
+    if (sync) __syncthreads();
   };
 
-  // prologue: blocks 0 and 1 in LDS, block 2 staged, S/dP of block 0
-  if (NB > 0) {
-    load_stage(0);
-    write_tiles(0);
-    write_vec(0);
+  // prologue: blocks 0 .. 2 in LDS, block 3 staged, S/dP of block 0
+#pragma unroll
+  for (int b0 = 0; b0 < 3; ++b0) {
+    if (NB > b0) {
+      load_stage(b0);
+      write_tiles(b0);
+      write_vec(b0);
+    }
   }
-  if (NB > 1) {
-    load_stage(1);
-    write_tiles(1);
-    write_vec(1);
-  }
-  if (NB > 2) load_stage(2);
+  if (NB > 3) load_stage(3);
   __syncthreads();
   if (NB > 0 && active(0)) {
 #pragma unroll
     for (int st = 0; st < NST1; ++st) step(fetch(-1, st), st, pB, dsB, sA, dpA);
   }
   for (int b = 0; b <= NB; b += 2) {
-    iteration(b, sA, dpA, sB, dpB, pB, dsB, pA, dsA);
-    if (b + 1 <= NB) iteration(b + 1, sB, dpB, sA, dpA, pA, dsA, pB, dsB);
+    iteration(b, sA, dpA, sB, dpB, pB, dsB, pA, dsA, false);
+    if (b + 1 <= NB) iteration(b + 1, sB, dpB, sA, dpA, pA, dsA, pB, dsB, true);
   }
 
   if (kj >= Nkv) return;
