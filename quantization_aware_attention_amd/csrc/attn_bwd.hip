@@ -356,11 +356,12 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 //                    packed as the next iteration's operands,
 // in eight fenced groups of MFMAs plus a slice of the vector work, so the
 // matrix core runs under the vector work of the same wave.  Q/dO blocks are
-// staged through registers: loaded from HBM in iteration b-4, written to LDS
-// slot b%8 in iteration b-3, read in iterations b-1 .. b+1.  A barrier ends
-// every odd iteration only: a block written in iteration c is first read in
-// c + 2, after the barrier that ends c or c + 1, and the block its slot held
-// before was last read in c - 4, two barriers earlier.
+// staged through registers: loaded from HBM in iteration b-5, written to LDS
+// slot b%8 in iteration b-4, read in iterations b-1 .. b+1.  A barrier ends
+// every third iteration only (b % 3 == 2): a block written in iteration c is
+// first read in c + 3, after a barrier that ends one of c .. c + 2, and the
+// block its slot held before was last read in c - 3, before a barrier that
+// ends one of c - 3 .. c - 1.
 constexpr int DSP_BN = 128;    // keys per workgroup
 constexpr int DSP_BQ = 32;     // queries per block
 constexpr int DSP_SLOTS = 8;   // LDS block slots
@@ -634,15 +635,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
     const bool do1 = b + 1 < NB && active(b + 1);
     const bool dov = b < NB && active(b);
     const bool full = do2 && do1 && dov;
-    // staging of block b+3 (loaded in iteration b-1) and loads of block b+4:
+    // staging of block b+4 (loaded in iteration b-1) and loads of block b+5:
     // inside the first fenced groups on the full path, up front otherwise
-    const bool stw = b + 3 < NB, stl = b + 4 < NB;
+    const bool stw = b + 4 < NB, stl = b + 5 < NB;
     if (!full) {
       if (stw) {
-        write_tiles(b + 3);
-        write_vec(b + 3);
+        write_tiles(b + 4);
+        write_vec(b + 4);
       }
-      if (stl) load_stage(b + 4);
+      if (stl) load_stage(b + 5);
     }
     if (dov) {   // masked scores -> -inf before the exponent
       const int q0 = qstart(b);
@@ -669,9 +670,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
           step(cur, st, Pp, DSp, S2, DP2);
         }
         valu_piece(j, b, S, DP, Pn, DSn);
-        if (j == 0 && stw) write_tiles(b + 3);
-        if (j == 1 && stw) write_vec(b + 3);
-        if (j == 2 && stl) load_stage(b + 4);
+        if (j == 0 && stw) write_tiles(b + 4);
+        if (j == 1 && stw) write_vec(b + 4);
+        if (j == 2 && stl) load_stage(b + 5);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
@@ -691,24 +692,24 @@ __global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
     if (sync) __syncthreads();
   };
 
-  // prologue: blocks 0 .. 2 in LDS, block 3 staged, S/dP of block 0
+  // prologue: blocks 0 .. 3 in LDS, block 4 staged, S/dP of block 0
 #pragma unroll
-  for (int b0 = 0; b0 < 3; ++b0) {
+  for (int b0 = 0; b0 < 4; ++b0) {
     if (NB > b0) {
       load_stage(b0);
       write_tiles(b0);
       write_vec(b0);
     }
   }
-  if (NB > 3) load_stage(3);
+  if (NB > 4) load_stage(4);
   __syncthreads();
   if (NB > 0 && active(0)) {
 #pragma unroll
     for (int st = 0; st < NST1; ++st) step(fetch(-1, st), st, pB, dsB, sA, dpA);
   }
   for (int b = 0; b <= NB; b += 2) {
-    iteration(b, sA, dpA, sB, dpB, pB, dsB, pA, dsA, false);
-    if (b + 1 <= NB) iteration(b + 1, sB, dpB, sA, dpA, pA, dsA, pB, dsB, true);
+    iteration(b, sA, dpA, sB, dpB, pB, dsB, pA, dsA, b % 3 == 2);
+    if (b + 1 <= NB) iteration(b + 1, sB, dpB, sA, dpA, pA, dsA, pB, dsB, (b + 1) % 3 == 2);
   }
 
   if (kj >= Nkv) return;
