@@ -388,6 +388,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float m_s[DSP_SLOTS][DSP_BQ];
   __shared__ __attribute__((aligned(16))) float d_s[DSP_SLOTS][DSP_BQ];
   __shared__ __attribute__((aligned(16))) float sq_s[DSP_SLOTS][DSP_BQ];
+  __shared__ __attribute__((aligned(16))) float cq_s[QKS ? DSP_SLOTS : 1][DSP_BQ];   // c * s_q (exponent scale)
   __shared__ __attribute__((aligned(16))) float qs_s[DSP_SLOTS][NGW][DSP_BQ];
   __shared__ __attribute__((aligned(16))) float qr_s[DSP_SLOTS][NGW][DSP_BQ];
 
@@ -504,7 +505,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
     const bool ok = e_used && qstart(b) + e_q < Nq;
     if (e_kind == 0) m_s[slot][e_q] = ok ? stv * LOG2E : 0.0f;
     else if (e_kind == 1) d_s[slot][e_q] = ok ? stv : 0.0f;
-    else if (e_kind == 2) sq_s[slot][e_q] = ok ? stv : 1.0f;
+    else if (e_kind == 2) {
+      sq_s[slot][e_q] = ok ? stv : 1.0f;
+      // a zero scale (all-zero row) is raised to the smallest normal so that a
+      // masked score stays -inf after the product
+      if constexpr (QKS) cq_s[slot][e_q] = a.c * fmaxf(ok ? stv : 1.0f, 1.17549435e-38f);
+    }
     else if (PQ >= 0 && e_kind < 3 + NGW) {
       const FqScale fs = fq_scale<FQF>(ok ? stv : 0.0f);
       qs_s[slot][e_kind - 3][e_q] = fs.s;
@@ -565,13 +571,16 @@ __global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
   // per-query vectors, form P, then quantize, form dS and pack both operands.
   // The reads of a quarter are issued a group or more before their use.
   float p[16];
-  f32x4 mvv[4], dvv[4], sqv[4], svv[4], rvv[4];
+  f32x4 mvv[4], dvv[4], sqv[4], cqv[4], svv[4], rvv[4];
   auto readvec = [&](int u, int b) __attribute__((always_inline)) {
     const int slot = b & (DSP_SLOTS - 1), ql = 8 * u + 4 * g;
     mvv[u] = *reinterpret_cast<const f32x4*>(&m_s[slot][ql]);
     dvv[u] = *reinterpret_cast<const f32x4*>(&d_s[slot][ql]);
     sqv[u] = (f32x4){1.0f, 1.0f, 1.0f, 1.0f};
-    if constexpr (QKS) sqv[u] = *reinterpret_cast<const f32x4*>(&sq_s[slot][ql]);
+    if constexpr (QKS) {
+      sqv[u] = *reinterpret_cast<const f32x4*>(&sq_s[slot][ql]);
+      cqv[u] = *reinterpret_cast<const f32x4*>(&cq_s[slot][ql]);
+    }
     if constexpr (PQ >= 0) {
       svv[u] = *reinterpret_cast<const f32x4*>(&qs_s[slot][lgrp][ql]);
       rvv[u] = *reinterpret_cast<const f32x4*>(&qr_s[slot][lgrp][ql]);
@@ -582,7 +591,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * u + e;
       const float sr = QKS ? S[r] * sk_lane : S[r];
-      const float cr = QKS ? a.c * fmaxf(sqv[u][e], 1.17549435e-38f) : a.c;
+      const float cr = QKS ? cqv[u][e] : a.c;
       p[r] = fast_exp2(__builtin_fmaf(sr, cr, -mvv[u][e]));
     }
   };
