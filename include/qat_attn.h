@@ -140,7 +140,9 @@ int qat_attn_bwd(const qat_attn_dims* dims, const void* q, const void* k, const 
  * qat_attn_bwd; `stages` is a mask of
  *   QAT_BWD_PREPARE  K smoothing and Q/K/V fake quant into the workspace
  *                    (QAT_SMOOTH_K, QAT_QKV_QUANT)
- *   QAT_BWD_DELTA    Delta = rowsum(dout o o_hp) into the workspace
+ *   QAT_BWD_DELTA    Delta = rowsum(dout o o_hp) into the workspace (together
+ *                    with QAT_BWD_DQ the dQ kernel forms it, the same bits,
+ *                    and no separate pass runs)
  *   QAT_BWD_DQ       dq, and the per-(row, 64-key group) P absmax into the
  *                    workspace (QAT_P_QUANT)
  *   QAT_BWD_DKDV     dk, dv (reads Delta and the P absmax)

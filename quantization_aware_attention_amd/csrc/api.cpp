@@ -217,9 +217,13 @@ int qat_attn_bwd_stages(const qat_attn_dims* dims, const void* q, const void* k,
   float* delta = reinterpret_cast<float*>(ws + L.delta);
   float* amax = (quant_flags & QAT_P_QUANT) ? reinterpret_cast<float*>(ws + L.amax) : nullptr;
   const int pfmt = pfmt_of(quant_flags);
-  if (stages & QAT_BWD_DELTA) QAT_TRY(qat::launch_bwd_delta(s, o_hp, dout, delta, st));
+  // Delta together with dQ: the dQ kernel forms it for its rows (bit for bit
+  // as the separate pass) and publishes it for dK/dV, one launch fewer
+  const bool delta_in_dq = (stages & QAT_BWD_DELTA) && (stages & QAT_BWD_DQ);
+  if ((stages & QAT_BWD_DELTA) && !delta_in_dq) QAT_TRY(qat::launch_bwd_delta(s, o_hp, dout, delta, st));
   if (stages & QAT_BWD_DQ)
-    QAT_TRY(qat::launch_bwd_dq(s, in, dout, lse, delta, sm_scale, causal != 0, pfmt, dq, amax, st));
+    QAT_TRY(qat::launch_bwd_dq(s, in, dout, lse, delta, delta_in_dq ? o_hp : nullptr, sm_scale, causal != 0, pfmt,
+                               dq, amax, st));
   if (stages & QAT_BWD_DKDV)
     QAT_TRY(qat::launch_bwd_dkdv(s, in, dout, lse, delta, amax, sm_scale, causal != 0, pfmt, dk, dv,
                                  reinterpret_cast<float*>(ws + L.part), st));

@@ -46,14 +46,17 @@ __global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__
     const u32x4 wb = *reinterpret_cast<const u32x4*>(b);
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      acc += DT::to_f32((uint16_t)(wa[e >> 1] >> (16 * (e & 1)))) * DT::to_f32((uint16_t)(wb[e >> 1] >> (16 * (e & 1))));
+      acc = __builtin_fmaf(DT::to_f32((uint16_t)(wa[e >> 1] >> (16 * (e & 1)))),
+                           DT::to_f32((uint16_t)(wb[e >> 1] >> (16 * (e & 1)))), acc);
   } else {
     const u32x2 wa = *reinterpret_cast<const u32x2*>(a);
     const u32x2 wb = *reinterpret_cast<const u32x2*>(b);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      acc += DT::to_f32((uint16_t)(wa[e >> 1] >> (16 * (e & 1)))) * DT::to_f32((uint16_t)(wb[e >> 1] >> (16 * (e & 1))));
+      acc = __builtin_fmaf(DT::to_f32((uint16_t)(wa[e >> 1] >> (16 * (e & 1)))),
+                           DT::to_f32((uint16_t)(wb[e >> 1] >> (16 * (e & 1)))), acc);
   }
+  // (the dQ kernel reproduces this order when it forms Delta itself: row_delta)
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
   if (row < rows && sub == 0) delta[row] = acc;
@@ -94,6 +97,8 @@ struct BwdArgs {
   void* dv;
   float* dkdv_part;     // fp32 partial dK/dV of split key blocks
   const float* k_mean;  // K smoothing: dQ += rowsum(dS) k_mean (null: off)
+  const void* o_hp;     // dQ: with delta_out, Delta is formed in the kernel
+  float* delta_out;     //   from o_hp and dout and written here
   int n_whole;          // dK/dV: key blocks run whole by one workgroup each
   int n_split;          // dK/dV: query-range parts of each remaining key block
   int Nq, Nkv, NG;
@@ -103,6 +108,52 @@ struct BwdArgs {
 
 
 // ------------------------------------------------------------------ dQ
+// Delta of one query row from the dQ kernel's operand layout (lane half g
+// holds d = 16 ks + 8 g + j, j = 0..7), in exactly delta_kernel's order: 16
+// chunks of D/16 consecutive products summed in sequence (each product of two
+// 16-bit values is exact in fp32), then pair sums of chunks 8, 4, 2 and 1
+// apart.  At D = 128 chunk 2 ks + g is one fragment and only the last pair
+// step crosses lane halves; at D = 64 chunk 4 ks + 2 g + h is half a fragment
+// and the step at distance 2 crosses.  Float addition commutes, so the
+// symmetric exchanges reproduce every partial sum bit for bit.
+template <class DT, int D>
+__device__ __forceinline__ float row_delta(const s16x8 (&ohf)[D / 16], const s16x8 (&dof)[D / 16]) {
+  constexpr int NKS = D / 16;
+  float t[NKS][2];   // chunk sums: [ks][half of the fragment] (D = 128 uses the whole fragment)
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const u32x4 wa = __builtin_bit_cast(u32x4, ohf[ks]), wb = __builtin_bit_cast(u32x4, dof[ks]);
+    float acc[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int h = D == 128 ? 0 : (j >> 2);
+      acc[h] = __builtin_fmaf(DT::to_f32((uint16_t)(wa[j >> 1] >> (16 * (j & 1)))),
+                              DT::to_f32((uint16_t)(wb[j >> 1] >> (16 * (j & 1)))), acc[h]);
+    }
+    t[ks][0] = acc[0];
+    t[ks][1] = acc[1];
+  }
+  if constexpr (D == 128) {   // chunk c = 2 ks + g
+    float s1[4], s2[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s1[i] = t[i][0] + t[i + 4][0];   // distance 8
+#pragma unroll
+    for (int i = 0; i < 2; ++i) s2[i] = s1[i] + s1[i + 2];       // distance 4
+    return sum_xor32(s2[0] + s2[1]);                             // distance 2, then 1 (lane halves)
+  } else {                    // chunk c = 4 ks + 2 g + h
+    float s1[2][2], s2[2], s3[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) s1[i][h] = t[i][h] + t[i + 2][h];   // distance 8
+#pragma unroll
+    for (int h = 0; h < 2; ++h) s2[h] = s1[0][h] + s1[1][h];         // distance 4
+#pragma unroll
+    for (int h = 0; h < 2; ++h) s3[h] = sum_xor32(s2[h]);            // distance 2 (lane halves)
+    return s3[0] + s3[1];                                            // distance 1
+  }
+}
+
 constexpr int DQ_BM = 128;
 constexpr int DQ_BN = 64;
 
@@ -143,7 +194,23 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
     const bool ok = qi < Nq;
     qf[ks] = ok ? *reinterpret_cast<const s16x8*>(qp + (size_t)qi * D + 16 * ks + 8 * g) : (s16x8){};
     dof[ks] = ok ? *reinterpret_cast<const s16x8*>(dop + (size_t)qi * D + 16 * ks + 8 * g) : (s16x8){};
-    if constexpr (VFP8) {   // dP = (dO * v_scale) code^T: the per-channel V scale moves onto dO
+  }
+  const float Mi = qi < Nq ? a.lse[(size_t)bh * Nq + qi] * LOG2E : 0.0f;
+  float Di;
+  if (a.delta_out) {   // Delta of this row (from dO as given), bit for bit as delta_kernel forms it, published for dK/dV
+    s16x8 ohf[NKS];
+    const uint16_t* ohp = (const uint16_t*)a.o_hp + (size_t)bh * Nq * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      ohf[ks] = qi < Nq ? *reinterpret_cast<const s16x8*>(ohp + (size_t)qi * D + 16 * ks + 8 * g) : (s16x8){};
+    Di = row_delta<DT, D>(ohf, dof);
+    if (g == 0 && qi < Nq) a.delta_out[(size_t)bh * Nq + qi] = Di;
+  } else {
+    Di = qi < Nq ? a.delta[(size_t)bh * Nq + qi] : 0.0f;
+  }
+  if constexpr (VFP8) {   // dP = (dO * v_scale) code^T: the per-channel V scale moves onto dO
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
       const f32x4 s0 = *reinterpret_cast<const f32x4*>(vsc + 16 * ks + 8 * g);
       const f32x4 s1 = *reinterpret_cast<const f32x4*>(vsc + 16 * ks + 8 * g + 4);
       const float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
@@ -156,8 +223,6 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
       dof[ks] = __builtin_bit_cast(s16x8, ws);
     }
   }
-  const float Mi = qi < Nq ? a.lse[(size_t)bh * Nq + qi] * LOG2E : 0.0f;
-  const float Di = qi < Nq ? a.delta[(size_t)bh * Nq + qi] : 0.0f;
   float c_row = a.c;   // IN_QKS: s_q folds into the log2 scale (same rounding as dK/dV)
   // (a zero scale, all-zero row, is raised to the smallest normal so that a
   // masked score stays -inf after the product)
@@ -845,11 +910,15 @@ static BwdArgs make_args(const Shape& s, const Inputs& in, const void* dout, con
 }
 
 hipError_t launch_bwd_dq(const Shape& s, const Inputs& in, const void* dout, const float* lse,
-                         const float* delta, float sm_scale, bool causal, int pfmt,
+                         float* delta, const void* o_hp, float sm_scale, bool causal, int pfmt,
                          void* dq, float* p_amax, hipStream_t st) {
   BwdArgs a = make_args(s, in, dout, lse, delta, sm_scale);
   a.dq = dq;
   a.p_amax = p_amax;
+  if (o_hp) {
+    a.o_hp = o_hp;
+    a.delta_out = delta;
+  }
   dim3 grid(((s.Nq + DQ_BM - 1) / DQ_BM) * s.B * s.H);
   return pick_all<DqK>(s, grid, a, causal, pfmt, in.mode, st);
 }

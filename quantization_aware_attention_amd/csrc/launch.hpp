@@ -76,8 +76,10 @@ hipError_t launch_fq_scale_selftest(int fmt, uint32_t* mismatches, hipStream_t s
 // Backward pieces.
 hipError_t launch_bwd_delta(const Shape& s, const void* o_hp, const void* dout, float* delta,
                             hipStream_t st);
+// o_hp non-null: the kernel forms Delta itself (as launch_bwd_delta would) and
+// writes it to delta; null: it reads delta.
 hipError_t launch_bwd_dq(const Shape& s, const Inputs& in, const void* dout, const float* lse,
-                         const float* delta, float sm_scale, bool causal, int pfmt,
+                         float* delta, const void* o_hp, float sm_scale, bool causal, int pfmt,
                          void* dq, float* p_amax, hipStream_t st);
 // part_ws: fp32 scratch of dkdv_part_bytes(s) for the partial sums of key
 // blocks split over query ranges (null: no block is split).

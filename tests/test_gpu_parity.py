@@ -85,6 +85,37 @@ def test_deterministic_bitwise():
         assert np.array_equal(a[n], b[n]), n
 
 
+@pytest.mark.parametrize("w", [BASE.with_(B=1, H=2, Nq=300, Nkv=260, seed=33),
+                               BASE.with_(B=1, H=2, Nq=150, Nkv=200, D=64, dtype="fp16", causal=False, seed=34),
+                               BASE.with_(B=2, H=1, Nq=200, Nkv=200, causal=True, qkv_quant=True, seed=35),
+                               W.WORKLOADS["cross_fp8v"].with_(B=1, H=2, Nq=150, Nkv=300, seed=36)],
+                         ids=["bf16_d128", "fp16_d64", "causal_qkv_quant", "fp8v"])
+def test_backward_stages_match_the_whole_backward_bitwise(w):
+    # With Delta and dQ in one call the dQ kernel forms Delta itself; run as
+    # separate stages, the Delta pass does.  dK/dV read that Delta, so equal
+    # bits everywhere show that both form it identically.
+    from quantization_aware_attention_amd import ops
+    from tests._harness import flags_of, to_dev, to_np
+    print(f"stage split case: {w}", flush=True)
+    inp = W.make_inputs(w)
+    q, k, v, do = (to_dev(inp[n + "_bits"], w.dtype) for n in ("q", "k", "v", "do"))
+    flags = flags_of(w, True)
+    v_scale = None
+    if w.v_fp8:
+        v, v_scale = ops.quant_v_fp8(v)
+    o, o_hp, lse = ops.attn_fwd(q, k, v, w.sm_scale, w.causal, flags, v_scale=v_scale)
+    whole = ops.attn_bwd(q, k, v, o_hp, lse, do, w.sm_scale, w.causal, flags, v_scale=v_scale)
+    dims = ops.dims_of(q, k)
+    ws = torch.zeros(max(ops.workspace_bytes(dims, flags, 1), 256), device="cuda", dtype=torch.uint8)
+    out = (torch.empty_like(q), torch.empty_like(k), torch.empty(k.shape, device="cuda", dtype=q.dtype))
+    for st in (ops.QAT_BWD_PREPARE | ops.QAT_BWD_DELTA, ops.QAT_BWD_DQ, ops.QAT_BWD_DKDV):
+        ops.attn_bwd(q, k, v, o_hp, lse, do, w.sm_scale, w.causal, flags, v_scale=v_scale, out=out, workspace=ws,
+                     stages=st)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), whole, out):
+        assert np.array_equal(to_np(a), to_np(b)), name
+
+
 def test_empty_batch_is_a_no_op():
     from quantization_aware_attention_amd import ops
     q = torch.zeros((0, 2, 16, 64), dtype=torch.bfloat16, device="cuda")
