@@ -102,7 +102,8 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, copy_mib: int):
     alg = {
         "fwd_kernel": BH * (w.Nq + 2 * w.Nkv) * w.D * e + BH * w.Nq * (2 * w.D * e + 4),
         "delta_kernel": BH * w.Nq * (2 * w.D * e + 4),
-        "dq_kernel": BH * (2 * w.Nq * w.D * e + 2 * w.Nkv * w.D * e + 8 * w.Nq) + BH * w.Nq * w.D * e,
+        # the step's dQ call also reads O_hp (it forms Delta; Delta is written instead of read)
+        "dq_kernel": BH * (3 * w.Nq * w.D * e + 2 * w.Nkv * w.D * e + 8 * w.Nq) + BH * w.Nq * w.D * e,
         "dkdv_kernel": BH * (2 * w.Nq * w.D * e + 2 * w.Nkv * w.D * e + 8 * w.Nq) + 2 * BH * w.Nkv * w.D * e,
     }
     out = {"workload": workload, "source_hash": kernel_source_hash(),
