@@ -177,6 +177,38 @@ def test_full_size_sampled(name):
     assert colsum.max() < 2e-2
 
 
+def _run_on_device(w, inp):
+    """Forward + backward as run_gpu does, outputs left on the device."""
+    from quantization_aware_attention_amd import ops
+    from tests._harness import flags_of, to_dev
+    q, k, v, do = (to_dev(inp[n + "_bits"], w.dtype) for n in ("q", "k", "v", "do"))
+    flags = flags_of(w, True)
+    v_scale = None
+    if w.v_fp8:
+        v, v_scale = ops.quant_v_fp8(v)
+    o, o_hp, lse = ops.attn_fwd(q, k, v, w.sm_scale, w.causal, flags, v_scale=v_scale)
+    dq, dk, dv = ops.attn_bwd(q, k, v, o_hp, lse, do, w.sm_scale, w.causal, flags, v_scale=v_scale)
+    torch.cuda.synchronize()
+    return {"o": o, "o_hp": o_hp, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+
+
+@pytest.mark.parametrize("name", ["dit_image", "long_video", "causal_lm", "cross_fp8v", "dit_image_smoothk"])
+def test_full_size_reruns_bitwise(name):
+    # The kernels' barriers follow hazard arguments (the forward syncs after
+    # every other phase, dK/dV after every third query block); at full size,
+    # with every compute unit busy and waves drifting apart, a missing
+    # ordering would show as differences between identical runs.
+    w, _ = FULL[name]
+    print(f"rerun case {name} full size: {w}", flush=True)
+    inp = W.make_inputs(w)
+    first = _run_on_device(w, inp)
+    for _ in range(2):
+        again = _run_on_device(w, inp)
+        for n, t in first.items():
+            assert torch.equal(t, again[n]), n
+        del again
+
+
 def test_smoothing_equals_plain_on_shifted_keys():
     """K = K0 + c with every channel of K0 made of +/- pairs on a 1/8 grid and
     c on a 1/4 grid: the mean over batch, heads and tokens is exactly c in any
