@@ -304,9 +304,9 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   constexpr int NKS = D / 16;
   constexpr int FQF = PQ >= 0 ? PQ : 0;
   constexpr int NPV = 4 * NDB;   // P@V steps of an MFMA phase
-  // fragments in flight ahead of their MFMAs (per-token codes: fewer, whose
-  // registers keep that variant free of most spills)
-  constexpr int PP_AHEAD = QKS ? 4 : 6;
+  // fragments in flight ahead of their MFMAs: five (no spills; six spilled
+  // and ran slower), four with per-token codes (which need more registers)
+  constexpr int PP_AHEAD = QKS ? 4 : 5;
   __shared__ __attribute__((aligned(16))) char kbuf[2][TILE];
   __shared__ __attribute__((aligned(16))) char vbuf[2][TILE];
   __shared__ __attribute__((aligned(16))) float ks_s[3][FWD_BN];   // IN_QKS: key scales of K(t)
