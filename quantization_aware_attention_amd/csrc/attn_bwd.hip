@@ -929,10 +929,12 @@ size_t dkdv_part_bytes(const Shape& s) {
   return (size_t)slots * 2 * DSP_BN * s.D * sizeof(float);
 }
 
-// Tail split: with U key blocks on C compute units, the last U mod C blocks
-// would run in a round of their own.  When they fill at most half of it,
-// each is cut into n_split query ranges (as many as fit in that round, at
-// most DKDV_MAX_SPLIT) whose partial sums a merge kernel adds up.  Causal
+// Tail split: with U key blocks on C compute units, the last rem = U mod C
+// blocks would run in a round of their own, mostly or partly idle.  They are
+// cut into k query ranges each (2 <= k <= DKDV_MAX_SPLIT), whose partial sums
+// a merge kernel adds up, with the k whose ceil(rem k / C) rounds of 1/k of
+// a block finish first (the smaller k on a tie): 96 leftover blocks of 256
+// take k = 2 (half a round), 192 take k = 4 (three quarter rounds).  Causal
 // launches already order their blocks longest first and are left whole.
 static void plan_dkdv(const Shape& s, bool causal, int cus, BwdArgs* a) {
   const int nkb = (s.Nkv + DSP_BN - 1) / DSP_BN;
@@ -942,13 +944,19 @@ static void plan_dkdv(const Shape& s, bool causal, int cus, BwdArgs* a) {
   a->n_split = 1;
   if (causal || cus <= 0 || !a->dkdv_part) return;
   const int rem = units % cus;
-  if (rem == 0 || 2 * rem > cus) return;
-  int split = cus / rem;
-  if (split > DKDV_MAX_SPLIT) split = DKDV_MAX_SPLIT;
-  if (split > nqb) split = nqb;
-  if (split < 2 || (long long)rem * split > DKDV_PART_SLOTS) return;
+  if (rem == 0) return;
+  int best = 1, best_rounds = 1;   // rounds of 1/best of a block: compare rounds / k across k
+  for (int k = 2; k <= DKDV_MAX_SPLIT && k <= nqb; ++k) {
+    if ((long long)rem * k > DKDV_PART_SLOTS) break;
+    const int rounds = (rem * k + cus - 1) / cus;
+    if (rounds * best < best_rounds * k) {   // rounds / k < best_rounds / best
+      best = k;
+      best_rounds = rounds;
+    }
+  }
+  if (best < 2) return;
   a->n_whole = units - rem;
-  a->n_split = split;
+  a->n_split = best;
 }
 
 template <class DT, int D>

@@ -88,9 +88,10 @@ hipError_t launch_bwd_dkdv(const Shape& s, const Inputs& in, const void* dout, c
                            int pfmt, void* dk, void* dv, float* part_ws, hipStream_t st);
 
 // dK/dV tail split: at most DKDV_MAX_SPLIT query ranges per key block and
-// DKDV_PART_SLOTS partial blocks in all.
+// DKDV_PART_SLOTS partial blocks in all (three rounds of quarter blocks on
+// 256 compute units).
 constexpr int DKDV_MAX_SPLIT = 4;
-constexpr int DKDV_PART_SLOTS = 256;
+constexpr int DKDV_PART_SLOTS = 768;
 size_t dkdv_part_bytes(const Shape& s);
 
 }  // namespace qat

@@ -93,8 +93,8 @@ def test_workspace_layout():
     up = lambda x: -(-x // 256) * 256
     delta = up(2 * 3 * 100 * 4)
     amax = up(2 * 3 * 3 * 100 * 4)            # ceil(130 / 64) = 3 groups
-    # fp32 dK/dV partials: up to 4 query ranges per 128-key block, at most 256 in all
-    part = up(min(6 * 2 * 4, 256) * 2 * 128 * 128 * 4)
+    # fp32 dK/dV partials: up to 4 query ranges per 128-key block, at most 768 in all
+    part = up(min(6 * 2 * 4, 768) * 2 * 128 * 128 * 4)
     assert ops.workspace_bytes(d, 0, 1) == delta + part
     assert ops.workspace_bytes(d, ops.QAT_P_QUANT, 1) == delta + amax + part
     qkv = up(6 * 100 * 128 * 2) + 2 * up(6 * 130 * 128 * 2) + up(6 * 100 * 4) + up(6 * 130 * 4)
@@ -107,8 +107,8 @@ def test_workspace_layout():
     assert ops.workspace_bytes(d, ops.QAT_SMOOTH_K, 0) == sk + ksm
     assert ops.workspace_bytes(d, ops.QAT_P_QUANT | ops.QAT_SMOOTH_K, 1) == delta + amax + part + sk + ksm
     assert ops.workspace_bytes(d, ops.QAT_QKV_QUANT | ops.QAT_SMOOTH_K, 0) == sk + qkv
-    big = D(1, 24, 4608, 4608, 128, 0)        # 864 key blocks: capped at 256 partial blocks
-    assert ops.workspace_bytes(big, 0, 1) == up(24 * 4608 * 4) + up(256 * 2 * 128 * 128 * 4)
+    big = D(1, 24, 4608, 4608, 128, 0)        # 864 key blocks: capped at 768 partial blocks
+    assert ops.workspace_bytes(big, 0, 1) == up(24 * 4608 * 4) + up(768 * 2 * 128 * 128 * 4)
     assert ops.workspace_bytes(d, 0, 2) == 0
 
 
