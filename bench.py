@@ -155,7 +155,7 @@ def main():
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.copy_mib or 512)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the kernel runs on one "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the kernel runs on one "
               "GPU's share of the heads); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
