@@ -50,7 +50,7 @@ extern "C" {
 /* status codes */
 #define QAT_OK 0
 #define QAT_EINVAL 1        /* null pointer, bad size, unknown flag bit      */
-#define QAT_EUNSUPPORTED 2  /* valid request this build does not implement    */
+#define QAT_EUNSUPPORTED 2  /* valid request the library does not implement   */
 #define QAT_EWORKSPACE 3    /* workspace pointer null or smaller than needed  */
 #define QAT_EHIP 4          /* a kernel launch failed                         */
 
