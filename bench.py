@@ -14,8 +14,8 @@ Prints one JSON line (rank 0):
             recomputation in the split backward is not credited)
   roofline  the slowest kernel of the step, timed with HIP events on the
             stream it runs on, against the bf16 dense MFMA peak
-  cpu_baseline  the float64 oracle on a bounded sample (two heads) on the
-            host cores, scaled to TFLOP/s
+  cpu_baseline  the float64 oracle on a bounded sample (six of the 24 heads by
+            default) on the host cores, scaled to TFLOP/s
 """
 from __future__ import annotations
 
@@ -258,6 +258,14 @@ def main():
     split_ms = {"fwd": per_call(fwd, max(args.steps, 20)),
                 "bwd": per_call(bwd if C == 1 else bwd_chunked, max(args.steps, 20)),
                 "step": per_call(step, max(args.steps, 20))}
+    # host time to enqueue the timed loop's steps (no synchronisation inside):
+    # tells a host-bound timed window from a GPU-bound one
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    host_ms = (time.perf_counter() - h0) * 1e3 / args.steps
+    torch.cuda.synchronize()
 
     Wn = w.B * w.H * w.Nq * w.Nkv * w.D
     if w.causal:
@@ -330,18 +338,32 @@ def main():
         v_codes = vs = None
         if w.v_fp8:
             v_codes, vs = oracle.quantize_v_channels(sample["v"], "e5m2")
-        c0 = time.perf_counter()
         kw = dict(causal=w.causal, p_fmt=w.p_fmt, qkv_quant=w.qkv_quant, v_codes=v_codes, v_scale=vs,
                   smooth_k=w.smooth_k, dtype=w.dtype)
+        c0 = time.perf_counter()
         oracle.attention_forward(sample["q"], sample["k"], sample["v"], w.sm_scale, **kw)
-        oracle.attention_backward(sample["q"], sample["k"], sample["v"], sample["do"], w.sm_scale, **kw)
         c1 = time.perf_counter()
+        oracle.attention_backward(sample["q"], sample["k"], sample["v"], sample["do"], w.sm_scale, **kw)
+        c2 = time.perf_counter()
+        # the threads the oracle ran on: NumPy's BLAS pool (its matrix products
+        # are where the time goes; everything else is single-threaded)
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        cpu = {"value": round(credited / (w.B * w.H) * nh / (c1 - c0) / 1e12, 6), "unit": "TFLOP/s",
+        share = nh / (w.B * w.H)
+        cpu = {"value": round(credited * share / (c2 - c0) / 1e12, 6), "unit": "TFLOP/s",
                "cores": threads, "kind": "oracle",
-               "sample": f"{nh} of {w.B * w.H} heads, forward + backward, float64 NumPy, {c1 - c0:.1f} s"}
+               "sample": f"{nh} of {w.B * w.H} heads, forward + backward, float64 NumPy, {c2 - c0:.1f} s",
+               "host_cpu_count": os.cpu_count(), "blas_threads": threads,
+               "fwd_s": round(c1 - c0, 3), "bwd_s": round(c2 - c1, 3),
+               "fwd_tflops": round(6.0 * Wn * share / (c1 - c0) / 1e12, 6),
+               "bwd_tflops": round(10.0 * Wn * share / (c2 - c1) / 1e12, 6)}
 
     fa_conv = 14.0 * Wn / (ms_step * 1e-3) / 1e12
+    # forward, backward and step throughput from the per-call medians
+    # (credited 6W, 10W, 16W) and their share of the bf16 dense peak
+    passes = {}
+    for name, flop in (("fwd", 6.0 * Wn), ("bwd", 10.0 * Wn), ("step", 16.0 * Wn)):
+        tf = flop / (split_ms[name]["median"] * 1e-3) / 1e12
+        passes[name] = {"tflops": round(tf, 2), "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
     extra = {}
     if w.v_fp8:
         # the quantized P^V runs on the fp8 MFMA (twice the bf16 rate): the
@@ -369,7 +391,8 @@ def main():
                                f"{', Q/K/V fake-quant e4m3' if w.qkv_quant else ''}"
                                f"{', V e5m2' if w.v_fp8 else ''}",
                    "credited_flop_per_step": credited, "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-                   "fa_convention_tflops": round(fa_conv, 2), "call_ms": split_ms,
+                   "fa_convention_tflops": round(fa_conv, 2), "call_ms": split_ms, "per_pass": passes,
+                   "host_enqueue_ms_per_step": round(host_ms, 4),
                    **({"kv_chunks": C} if C > 1 else {}), **extra},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -195,8 +195,15 @@ int qat_attn_merge(const qat_attn_dims* dims, int n_chunks, const void* const* o
                    void* o, void* o_hp, float* lse, void* stream);
 int qat_attn_sum(const qat_attn_dims* dims, int n_parts, const void* const* parts, void* out, void* stream);
 
-/* Workspace bytes needed by the forward (pass 0) or the backward (pass 1);
- * 0 for invalid dims. */
+/*
+ * Workspace bytes needed by the forward (pass 0) or the backward (pass 1).
+ * No page defines this call: the FastVideo source's _attention.forward and
+ * _attention.backward allocate their scratch tensors themselves (the
+ * fake-quantized q, k, v copies, M, delta), while this library never
+ * allocates, so the caller asks for the size and passes the buffer in.
+ * Returns 0 for a null dims pointer, negative sizes or a pass other than
+ * 0 or 1; otherwise the size for these dims and flags (it may be 0).
+ */
 size_t qat_attn_workspace_bytes(const qat_attn_dims* dims, uint32_t quant_flags, int pass);
 
 /*
@@ -245,10 +252,22 @@ int qat_selftest_exp2_monotone(float lo, float hi, uint32_t* violations, void* s
  */
 int qat_selftest_fq_scale(int32_t fmt, uint32_t* mismatches, void* stream);
 
-/* QAT_ATTN_P_GROUP as compiled into the kernels. */
+/*
+ * QAT_ATTN_P_GROUP as compiled into the kernels: the number of key columns
+ * that share one P-quant scale per query row.  In the FastVideo source this
+ * is the BLOCK_SIZE_QUANT_DIM argument of the fake_quantize call on the P
+ * tile inside _attn_fwd_inner (the kernel's BLOCK_N, which differs between its
+ * forward and backward variants); here one width serves both passes.  No
+ * arguments, no errors.
+ */
 int qat_attn_p_group(void);
 
-/* Static description of a status code. */
+/*
+ * Static description of a status code (never NULL; "unknown status" for a
+ * value that is not one of the QAT_* codes).  No page defines it: the
+ * source reports errors through Python exceptions (assert, ValueError in
+ * _attention.forward); the C boundary returns codes instead.
+ */
 const char* qat_attn_strerror(int status);
 
 #ifdef __cplusplus

@@ -64,8 +64,6 @@ on the pages):
 """
 from __future__ import annotations
 
-import math
-
 import numpy as np
 
 from . import fp8
@@ -394,16 +392,3 @@ def merge_chunks(o_parts, o_hp_parts, lse_parts):
     O = sum(wn[c][..., None] * np.asarray(o_parts[c], dtype=np.float64) for c in range(len(o_parts)))
     O_hp = sum(wn[c][..., None] * np.asarray(o_hp_parts[c], dtype=np.float64) for c in range(len(o_parts)))
     return O, O_hp, lse
-
-
-def flops_fwd_bwd(B, H, Nq, Nkv, D, causal=False):
-    """Credited work: forward 3 GEMMs (QK^T, P^V, P_hp V), backward 5."""
-    W = B * H * Nq * Nkv * D
-    if causal:
-        W = W * (Nq + 1) / (2 * Nq)
-    return 6 * W, 10 * W
-
-
-def default_sm_scale(D: int) -> float:
-    """1/sqrt(D) rounded to fp32, the softmax scale of every workload here."""
-    return float(np.float32(1.0 / math.sqrt(D)))

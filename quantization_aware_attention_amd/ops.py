@@ -103,11 +103,53 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _need(t, name, dtype=None):
-    if not (t.is_cuda and t.is_contiguous()):
-        raise ValueError(f"{name} must be a contiguous CUDA tensor")
+def _need(t, name, dtype=None, shape=None, device=None):
+    """Check a tensor handed to the library: the C ABI sees only raw pointers,
+    so a tensor of the wrong shape, dtype or device would become an
+    out-of-bounds device access instead of an error."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _on_device(**named):
+    """Last check, after every shape and dtype: the library takes device
+    pointers to contiguous storage only."""
+    for name, t in named.items():
+        if t is not None and not (t.is_cuda and t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous CUDA tensor")
+
+
+def _need_inputs(q, k, v, quant_flags, v_scale):
+    """q [B,H,Nq,D] (bf16/fp16), k [B,H,Nkv,D] and v (k's shape; uint8 codes
+    with QAT_V_FP8_E5M2, then v_scale fp32 [B,H,D]) on one device."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4 or q.dtype not in _DTYPES:
+        raise ValueError("q must be a 4-D bf16 or fp16 tensor [B, H, N, D]")
+    B, H, _, D = q.shape
+    if not isinstance(k, torch.Tensor) or k.dim() != 4:
+        raise ValueError("k must be a 4-D tensor [B, H, Nkv, D]")
+    kshape = (B, H, k.shape[2], D)
+    _need(k, "k", q.dtype, kshape, q.device)
+    fp8v = bool(quant_flags & QAT_V_FP8_E5M2)
+    _need(v, "v", torch.uint8 if fp8v else q.dtype, kshape, q.device)
+    if fp8v:
+        if v_scale is None:
+            raise ValueError("v_scale is required with QAT_V_FP8_E5M2")
+        _need(v_scale, "v_scale", torch.float32, (B, H, D), q.device)
+    elif v_scale is not None:
+        raise ValueError("v_scale is only used with QAT_V_FP8_E5M2")
+
+
+def _need_workspace(ws, q):
+    if ws is not None:
+        _need(ws, "workspace", torch.uint8, device=q.device)
+        if ws.dim() != 1:
+            raise ValueError("workspace must be a 1-D uint8 tensor")
 
 
 def dims_of(q, k):
@@ -127,11 +169,8 @@ def attn_fwd(q, k, v, sm_scale, causal=False, quant_flags=QAT_P_QUANT, v_scale=N
              out=None, workspace=None):
     """Forward: returns (o, o_hp, lse).  With QAT_V_FP8_E5M2, ``v`` is uint8
     e5m2 codes and ``v_scale`` fp32 [B, H, D]."""
-    _need(q, "q")
-    _need(k, "k", q.dtype)
-    _need(v, "v", torch.uint8 if quant_flags & QAT_V_FP8_E5M2 else q.dtype)
-    if v_scale is not None:
-        _need(v_scale, "v_scale", torch.float32)
+    _need_inputs(q, k, v, quant_flags, v_scale)
+    _need_workspace(workspace, q)
     dims = dims_of(q, k)
     if out is None:
         o = torch.empty_like(q)
@@ -139,6 +178,10 @@ def attn_fwd(q, k, v, sm_scale, causal=False, quant_flags=QAT_P_QUANT, v_scale=N
         lse = torch.empty(q.shape[:3], device=q.device, dtype=torch.float32)
     else:
         o, o_hp, lse = out
+        _need(o, "out[0] (o)", q.dtype, q.shape, q.device)
+        _need(o_hp, "out[1] (o_hp)", q.dtype, q.shape, q.device)
+        _need(lse, "out[2] (lse)", torch.float32, q.shape[:3], q.device)
+    _on_device(q=q, k=k, v=v, v_scale=v_scale, o=o, o_hp=o_hp, lse=lse, workspace=workspace)
     nbytes = workspace_bytes(dims, quant_flags, 0)
     if workspace is None and nbytes:
         workspace = torch.empty(nbytes, device=q.device, dtype=torch.uint8)
@@ -154,12 +197,11 @@ def attn_bwd(q, k, v, o_hp, lse, dout, sm_scale, causal=False, quant_flags=QAT_P
              v_scale=None, out=None, workspace=None, stages=QAT_BWD_ALL):
     """Straight-through backward: returns (dq, dk, dv).  ``stages`` selects a
     subset of the backward stages (qat_attn_bwd_stages)."""
-    _need(q, "q")
-    _need(k, "k", q.dtype)
-    _need(v, "v", torch.uint8 if quant_flags & QAT_V_FP8_E5M2 else q.dtype)
-    _need(o_hp, "o_hp", q.dtype)
-    _need(lse, "lse", torch.float32)
-    _need(dout, "dout", q.dtype)
+    _need_inputs(q, k, v, quant_flags, v_scale)
+    _need(o_hp, "o_hp", q.dtype, q.shape, q.device)
+    _need(lse, "lse", torch.float32, q.shape[:3], q.device)
+    _need(dout, "dout", q.dtype, q.shape, q.device)
+    _need_workspace(workspace, q)
     dims = dims_of(q, k)
     if out is None:
         dq = torch.empty_like(q)
@@ -167,6 +209,11 @@ def attn_bwd(q, k, v, o_hp, lse, dout, sm_scale, causal=False, quant_flags=QAT_P
         dv = torch.empty(k.shape, device=k.device, dtype=q.dtype)
     else:
         dq, dk, dv = out
+        _need(dq, "out[0] (dq)", q.dtype, q.shape, q.device)
+        _need(dk, "out[1] (dk)", q.dtype, k.shape, q.device)
+        _need(dv, "out[2] (dv)", q.dtype, k.shape, q.device)
+    _on_device(q=q, k=k, v=v, v_scale=v_scale, o_hp=o_hp, lse=lse, dout=dout, dq=dq, dk=dk, dv=dv,
+               workspace=workspace)
     nbytes = workspace_bytes(dims, quant_flags, 1)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 256), device=q.device, dtype=torch.uint8)
@@ -188,13 +235,23 @@ def _ptr_array(ts):
 def attn_merge(o_parts, o_hp_parts, lse_parts, out=None):
     """Merge the forward results of KV chunks by their log-sum-exp
     (qat_attn_merge): returns (o, o_hp, lse)."""
-    for i, (o, oh, l) in enumerate(zip(o_parts, o_hp_parts, lse_parts)):
-        _need(o, f"o_parts[{i}]")
-        _need(oh, f"o_hp_parts[{i}]", o_parts[0].dtype)
-        _need(l, f"lse_parts[{i}]", torch.float32)
+    if not (len(o_parts) == len(o_hp_parts) == len(lse_parts)) or not o_parts:
+        raise ValueError("o_parts, o_hp_parts and lse_parts must be non-empty lists of equal length")
     q0 = o_parts[0]
+    if not isinstance(q0, torch.Tensor) or q0.dim() != 4 or q0.dtype not in _DTYPES:
+        raise ValueError("o_parts[0] must be a 4-D bf16 or fp16 tensor [B, H, Nq, D]")
+    for i, (o, oh, l) in enumerate(zip(o_parts, o_hp_parts, lse_parts)):
+        _need(o, f"o_parts[{i}]", q0.dtype, q0.shape, q0.device)
+        _need(oh, f"o_hp_parts[{i}]", q0.dtype, q0.shape, q0.device)
+        _need(l, f"lse_parts[{i}]", torch.float32, q0.shape[:3], q0.device)
     o, o_hp, lse = out if out is not None else (torch.empty_like(q0), torch.empty_like(q0),
                                                 torch.empty(q0.shape[:3], dtype=torch.float32, device=q0.device))
+    _need(o, "out[0] (o)", q0.dtype, q0.shape, q0.device)
+    _need(o_hp, "out[1] (o_hp)", q0.dtype, q0.shape, q0.device)
+    _need(lse, "out[2] (lse)", torch.float32, q0.shape[:3], q0.device)
+    _on_device(**{f"o_parts[{i}]": x for i, x in enumerate(o_parts)},
+               **{f"o_hp_parts[{i}]": x for i, x in enumerate(o_hp_parts)},
+               **{f"lse_parts[{i}]": x for i, x in enumerate(lse_parts)}, o=o, o_hp=o_hp, lse=lse)
     dims = dims_of(q0, q0)
     _check("qat_attn_merge", lib().qat_attn_merge(ctypes.byref(dims), len(o_parts), _ptr_array(o_parts),
                                                   _ptr_array(o_hp_parts), _ptr_array(lse_parts), _ptr(o), _ptr(o_hp),
@@ -204,9 +261,16 @@ def attn_merge(o_parts, o_hp_parts, lse_parts, out=None):
 
 def attn_sum(parts, out=None):
     """Sum of [B, H, N, D] tensors in fp32, part order (qat_attn_sum)."""
+    if not parts:
+        raise ValueError("parts must be a non-empty list")
+    p0 = parts[0]
+    if not isinstance(p0, torch.Tensor) or p0.dim() != 4 or p0.dtype not in _DTYPES:
+        raise ValueError("parts[0] must be a 4-D bf16 or fp16 tensor [B, H, N, D]")
     for i, t in enumerate(parts):
-        _need(t, f"parts[{i}]", parts[0].dtype)
-    out = torch.empty_like(parts[0]) if out is None else out
+        _need(t, f"parts[{i}]", p0.dtype, p0.shape, p0.device)
+    out = torch.empty_like(p0) if out is None else out
+    _need(out, "out", p0.dtype, p0.shape, p0.device)
+    _on_device(**{f"parts[{i}]": x for i, x in enumerate(parts)}, out=out)
     dims = dims_of(parts[0], parts[0])
     _check("qat_attn_sum", lib().qat_attn_sum(ctypes.byref(dims), len(parts), _ptr_array(parts), _ptr(out),
                                               _stream()))
@@ -215,7 +279,9 @@ def attn_sum(parts, out=None):
 
 def quant_v_fp8(v):
     """Per-(b, h, d) e5m2 quantization of V: returns (codes uint8, v_scale fp32 [B, H, D])."""
-    _need(v, "v")
+    if not isinstance(v, torch.Tensor) or v.dim() != 4 or v.dtype not in _DTYPES:
+        raise ValueError("v must be a 4-D bf16 or fp16 tensor [B, H, N, D]")
+    _on_device(v=v)
     B, H, N, D = v.shape
     dims = Dims(B, H, 0, N, D, _DTYPES[v.dtype])
     codes = torch.empty(v.shape, device=v.device, dtype=torch.uint8)
@@ -226,7 +292,10 @@ def quant_v_fp8(v):
 
 def fake_quant_rows(x, group, fmt):
     """FQ of fp32 rows (fmt 0 = e4m3fn, 1 = e5m2): returns (codes, scales, xhat)."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-D float32 tensor [rows, cols]")
     _need(x, "x", torch.float32)
+    _on_device(x=x)
     rows, cols = x.shape
     ng = -(-cols // group)
     codes = torch.empty((rows, cols), device=x.device, dtype=torch.uint8)

@@ -15,8 +15,11 @@ from quantization_aware_attention_amd import ops
 
 @pytest.fixture(scope="module")
 def L():
+    # a fresh checkout has no library yet: build it (hipcc cross-compiles for
+    # gfx950 without a GPU) rather than skipping the boundary checks
     if not os.path.exists(ops.LIB_PATH):
-        pytest.skip("libqat_attn.so not built")
+        from quantization_aware_attention_amd import build
+        build.build()
     return ops.lib()
 
 

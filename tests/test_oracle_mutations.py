@@ -15,6 +15,7 @@ import oracle.qat_attention as qa_mod
 from tests import test_oracle_attention as TA
 from tests import test_oracle_fp8 as TF
 from tests import test_oracle_quant as TQ
+from tests import test_oracle_qkv_wiring as TW
 
 
 def _pins_attention():
@@ -40,6 +41,12 @@ def _pins_quant():
     yield TQ.test_groups_are_independent_and_absolute
     yield TQ.test_zero_and_underflow_groups
     yield TQ.test_token_and_channel_helpers
+
+
+def _pins_qkv():
+    for which in "qkv":
+        for causal in (False, True):
+            yield lambda w=which, c=causal: TW.test_qkv_quant_equals_attention_on_hand_quantized_inputs(w, c)
 
 
 def _pins_fp8():
@@ -70,6 +77,16 @@ MUTANTS = [
     (qa_mod, "fake_quant_groups", "a = np.max(np.abs(blk), axis=1)", "a = np.max(blk, axis=1)", "quant"),
     (qa_mod, "fake_quant_groups", "c0, c1 = g * group, min((g + 1) * group, cols)", "c0, c1 = g * group + (g > 0), min((g + 1) * group + 1, cols)", "quant"),
     (qa_mod, "quantize_v_channels", "fake_quant_groups(vt, fmt, N)", "fake_quant_groups(vt, fmt, max(1, N // 2))", "quant"),
+    # Q/K/V fake-quant wiring: a tensor left unquantized, the e5m2 grid, one
+    # scale per channel instead of per token
+    (qa_mod, "_prepare_head", 'vh = quantize_token_rows(vh, "e4m3")[2].astype(np.float64)', "vh = vh", "qkv"),
+    (qa_mod, "_prepare_head", 'qh = quantize_token_rows(qh, "e4m3")[2].astype(np.float64)', "qh = qh", "qkv"),
+    (qa_mod, "_prepare_head", 'qh = quantize_token_rows(qh, "e4m3")', 'qh = quantize_token_rows(qh, "e5m2")', "qkv"),
+    (qa_mod, "_prepare_head", 'kh = quantize_token_rows(kh, "e4m3")', 'kh = quantize_token_rows(kh, "e5m2")', "qkv"),
+    (qa_mod, "_prepare_head", 'kh = quantize_token_rows(kh, "e4m3")[2].astype(np.float64)',
+     'kh = quantize_token_rows(kh.T, "e4m3")[2].T.astype(np.float64)', "qkv"),
+    (qa_mod, "_prepare_head", 'vh = quantize_token_rows(vh, "e4m3")[2].astype(np.float64)',
+     'vh = quantize_token_rows(vh.T, "e4m3")[2].T.astype(np.float64)', "qkv"),
     (fp8_mod, "round_rne_sat", "n = np.rint(a / quantum)", "n = np.floor(a / quantum + 0.5)", "fp8"),
     (fp8_mod, "round_rne_sat", "e = np.maximum(ex - 1, emin)", "e = np.maximum(ex, emin)", "fp8"),
     (fp8_mod, "decode", "(1 - bias - mbits)", "(-bias - mbits)", "fp8"),
@@ -87,7 +104,7 @@ def _mutate(module, fname, old, new):
                          ids=lambda m: f"{m[1]}:{m[3][:40]}")
 def test_planted_mistake_is_caught(case):
     module, fname, old, new, family = case
-    pins = {"attn": _pins_attention, "quant": _pins_quant, "fp8": _pins_fp8}[family]
+    pins = {"attn": _pins_attention, "quant": _pins_quant, "fp8": _pins_fp8, "qkv": _pins_qkv}[family]
     try:
         _mutate(module, fname, old, new)
         caught = False
