@@ -27,6 +27,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <type_traits>
+
 namespace qat {
 
 // ------------------------------------------------------------------ Delta
@@ -407,58 +409,66 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Software-pipelined dK/dV: one wave per SIMD.
+// dK/dV in split roles: two waves per SIMD.
 //
-// Four waves own 128 keys (32 each) and produce dK and dV for them, walking
-// the query range in blocks of 32.  Each wave holds the whole 512-entry
-// register file: the dK/dV accumulators, the K and V operands of its keys,
-// two S/dP buffers and two sets of packed P^/dS operands.  Iteration b
-// issues as one instruction stream
-//   the matrix work  dV^T += dO^T P^(b-1), dK^T += Q^T dS(b-1),
-//                    S(b+1) = Q K^T, dP(b+1) = dO V^T, and
-//   the vector work of block b: P = exp2(S c - M), P^ = FQ(P) with the
-//                    (query, 64-key group) scales, dS = P o (dP - Delta),
-//                    packed as the next iteration's operands,
-// in eight fenced groups of MFMAs plus a slice of the vector work, so the
-// matrix core runs under the vector work of the same wave.  Q/dO blocks are
-// staged through registers: loaded from HBM in iteration b-5, written to LDS
-// slot b%8 in iteration b-4, read in iterations b-1 .. b+1.  A barrier ends
-// every third iteration only (b % 3 == 2): a block written in iteration c is
-// first read in c + 3, after a barrier that ends one of c .. c + 2, and the
-// block its slot held before was last read in c - 3, before a barrier that
-// ends one of c - 3 .. c - 1.
-constexpr int DSP_BN = 128;    // keys per workgroup
-constexpr int DSP_BQ = 32;     // queries per block
-constexpr int DSP_SLOTS = 8;   // LDS block slots
+// A workgroup of eight waves owns 128 keys and walks the query range in
+// blocks of 32.  Waves w < 4 ("P waves") and w + 4 ("dS waves") share a SIMD
+// and the same 32 keys (lane = key, so every product below is the operand
+// layout of the next one):
+//   P wave:  S = Q K^T, P = exp2(S c - M) (masks), P^ = FQ(P) with the
+//            (query, 64-key group) scales, dV^T += dO^T P^; it hands the
+//            high-precision P to its partner through LDS;
+//   dS wave: dP = dO V^T, dS = P o (dP - Delta) with that P,
+//            dK^T += Q^T dS.
+// Each wave holds one accumulator (dV or dK, 64 registers at D = 128) and one
+// of the K^T / V^T operands, which fits the 256 registers of two waves per
+// SIMD: while one wave waits on an MFMA or an LDS read the other issues, and
+// the two waves' vector work runs under each other's matrix work.
+// Iteration i (one workgroup barrier at its end):
+//   P wave:  S(i+1) MFMAs; vector work of block i (P(i) to LDS, P^(i));
+//            dV MFMAs of block i;
+//   dS wave: dP(i) MFMAs; vector work of block i-1 (P(i-1) from LDS, written
+//            in iteration i-1); dK MFMAs of block i-1;
+//   all:     block i+2 (loaded in iteration i-1) written to LDS slot
+//            (i+2) % 4, block i+3 loaded into registers.
+// LDS slot reads in iteration i touch blocks i-1 .. i+1 only, so the slot
+// written in iteration i was last read in iteration i-1, before the barrier;
+// the P buffer of parity i&1 is rewritten in iteration i+2, after the
+// barrier that ends the dS wave's read of it in iteration i+1.
+constexpr int DPR_BN = 128;    // keys per workgroup
+constexpr int DPR_BQ = 32;     // queries per block
+constexpr int DPR_SLOTS = 4;   // LDS slots of Q/dO blocks
 
 template <class DT, int D, bool CAUSAL, int PQ, int IN>
-__global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
   constexpr bool VFP8 = IN == IN_VFP8;
   constexpr bool QKS = IN == IN_QKS;
-  constexpr int TILE = DSP_BQ * D * 2;
+  constexpr int TILE = DPR_BQ * D * 2;
   constexpr int NDB = D / 32;
   constexpr int NKS = D / 16;
   constexpr int FQF = PQ >= 0 ? PQ : 0;
-  constexpr int NGW = DSP_BN / 64;          // 64-key P groups of the workgroup
+  constexpr int NGW = DPR_BN / 64;          // 64-key P groups of the workgroup
   constexpr int CPR = D / 8;                // 16-byte chunks per row
-  constexpr int NCH = DSP_BQ * CPR / 256;   // staged chunks per thread per tile
-  constexpr int NST2 = 4 * NDB;             // dV/dK MFMAs of a block
-  constexpr int NST = NST2 + 2 * NKS;       // + S/dP MFMAs
+  constexpr int CHUNKS = DPR_BQ * CPR;      // chunks per tensor and block
+  constexpr int NCH = 2 * CHUNKS / 512;     // staged chunks per thread (Q and dO together)
+  constexpr int NST = NKS + 2 * NDB;        // MFMA steps of a wave per iteration
   constexpr int NGRP = 8;                   // fenced groups per iteration
   constexpr int GSZ = NST / NGRP;           // MFMAs per group
-  constexpr int AHEAD = 4;                  // MFMA steps whose LDS operand is in flight
-  static_assert(NST % NGRP == 0 && NCH >= 1, "shape");
-  __shared__ __attribute__((aligned(16))) char q_s[DSP_SLOTS][TILE];
-  __shared__ __attribute__((aligned(16))) char do_s[DSP_SLOTS][TILE];
-  __shared__ __attribute__((aligned(16))) float m_s[DSP_SLOTS][DSP_BQ];
-  __shared__ __attribute__((aligned(16))) float d_s[DSP_SLOTS][DSP_BQ];
-  __shared__ __attribute__((aligned(16))) float sq_s[DSP_SLOTS][DSP_BQ];
-  __shared__ __attribute__((aligned(16))) float cq_s[QKS ? DSP_SLOTS : 1][DSP_BQ];   // c * s_q (exponent scale)
-  __shared__ __attribute__((aligned(16))) float qs_s[DSP_SLOTS][NGW][DSP_BQ];
-  __shared__ __attribute__((aligned(16))) float qr_s[DSP_SLOTS][NGW][DSP_BQ];
+  constexpr int AHEAD = 2;                  // MFMA steps whose LDS operand is in flight
+  static_assert(NST % NGRP == 0 && NCH >= 1 && 2 * CHUNKS % 512 == 0, "shape");
+  __shared__ __attribute__((aligned(16))) char q_s[DPR_SLOTS][TILE];
+  __shared__ __attribute__((aligned(16))) char do_s[DPR_SLOTS][TILE];
+  __shared__ __attribute__((aligned(16))) float m_s[DPR_SLOTS][DPR_BQ];
+  __shared__ __attribute__((aligned(16))) float d_s[DPR_SLOTS][DPR_BQ];
+  __shared__ __attribute__((aligned(16))) float sq_s[QKS ? DPR_SLOTS : 1][DPR_BQ];
+  __shared__ __attribute__((aligned(16))) float cq_s[QKS ? DPR_SLOTS : 1][DPR_BQ];   // c * s_q (exponent scale)
+  __shared__ __attribute__((aligned(16))) float qs_s[DPR_SLOTS][NGW][DPR_BQ];
+  __shared__ __attribute__((aligned(16))) float qr_s[DPR_SLOTS][NGW][DPR_BQ];
+  __shared__ __attribute__((aligned(16))) f32x4 p_s[2][4][4][64];   // [block parity][key quarter][reg quarter][lane]
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
-  const int nkb = (a.Nkv + DSP_BN - 1) / DSP_BN;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int kw = w & 3;   // this wave's 32 keys within the workgroup
+  const int nkb = (a.Nkv + DPR_BN - 1) / DPR_BN;
   // Workgroups [0, n_whole) take whole key blocks; the rest take one of
   // n_split query ranges of the last key blocks, which would otherwise run
   // alone in a last, mostly idle round of the chip.
@@ -476,69 +486,34 @@ __global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
     nparts = a.n_split;
   }
   const int bh = unit / nkb;
-  const int k0 = (unit % nkb) * DSP_BN;
-  const int k0w = k0 + w * 32;
+  const int k0 = (unit % nkb) * DPR_BN;
+  const int k0w = k0 + kw * 32;
   const int kj = k0w + l32;
   const int Nq = a.Nq, Nkv = a.Nkv;
-  const int lgrp = w >> 1;                // this wave's 64-key group within the workgroup
+  const int lgrp = kw >> 1;               // this wave's 64-key group within the workgroup
   const int grp0 = k0 / 64;
   const uint16_t* qp = (const uint16_t*)a.q + (size_t)bh * Nq * D;
   const uint16_t* dop = (const uint16_t*)a.dout + (size_t)bh * Nq * D;
-  const uint16_t* kp = (const uint16_t*)a.k + (size_t)bh * Nkv * D;
 
-  // K^T and V^T operands of this wave's 32 keys: lane holds key kj, d = 16ks + 8g .. +7
-  s16x8 kf[NKS], vf[NKS];
-  {
-    const bool ok = kj < Nkv;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      kf[ks] = ok ? *reinterpret_cast<const s16x8*>(kp + (size_t)kj * D + 16 * ks + 8 * g) : (s16x8){};
-      vf[ks] = (s16x8){};
-      if (ok) {
-        if constexpr (VFP8) {
-          const uint8_t* vp = (const uint8_t*)a.v + (size_t)bh * Nkv * D;
-          const float* vsc = a.v_scale + (size_t)bh * D + 16 * ks + 8 * g;
-          const u32x2 codes = *reinterpret_cast<const u32x2*>(vp + (size_t)kj * D + 16 * ks + 8 * g);
-          uint32_t wv[4];
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            const f32x2 f = __builtin_amdgcn_cvt_pk_f32_bf8((int)(codes[h >> 1] >> (16 * (h & 1))), false);
-            wv[h] = BF16::pack2(f[0] * vsc[2 * h], f[1] * vsc[2 * h + 1]);
-          }
-          vf[ks] = __builtin_bit_cast(s16x8, (u32x4){wv[0], wv[1], wv[2], wv[3]});
-        } else {
-          const uint16_t* vp = (const uint16_t*)a.v + (size_t)bh * Nkv * D;
-          vf[ks] = *reinterpret_cast<const s16x8*>(vp + (size_t)kj * D + 16 * ks + 8 * g);
-        }
-      }
-    }
-  }
-  // per-key scale in the exponent; raised to the smallest normal (and 1 for
-  // absent keys) so that a masked score stays -inf after the product
-  const float sk_lane = QKS ? (kj < Nkv ? fmaxf(a.k_scale[(size_t)bh * Nkv + kj], 1.17549435e-38f) : 1.0f) : 1.0f;
-  // these loads complete here, so that no wait for them lands inside the loop
-  // (where it would also drain the block loads in flight)
-  wait_vmem();
-
-  const int qb_first = CAUSAL ? k0 / DSP_BQ : 0;
-  const int nqb = (Nq + DSP_BQ - 1) / DSP_BQ;
+  const int qb_first = CAUSAL ? k0 / DPR_BQ : 0;
+  const int nqb = (Nq + DPR_BQ - 1) / DPR_BQ;
   const int NB_all = nqb > qb_first ? nqb - qb_first : 0;
   const int qb_begin = qb_first + NB_all * part / nparts;
   const int NB = qb_first + NB_all * (part + 1) / nparts - qb_begin;   // query blocks of this workgroup
   const bool wave_live = k0w < Nkv;
-  auto qstart = [&](int b) { return (qb_begin + b) * DSP_BQ; };
+  auto qstart = [&](int b) { return (qb_begin + b) * DPR_BQ; };
   // some (query, key) pair of block b and this wave's keys is unmasked
-  auto active = [&](int b) { return wave_live && (!CAUSAL || qstart(b) + DSP_BQ - 1 >= k0w); };
+  auto active = [&](int b) { return wave_live && (!CAUSAL || qstart(b) + DPR_BQ - 1 >= k0w); };
 
-  // ---- staging of a block: thread tid holds chunks tid + 256i of the Q and
-  // dO tiles and vector entry tid (kind tid/32: 0 LSE, 1 Delta, 2 query
-  // scale, 3.. P-quant absmax of local group kind-3; query tid%32)
-  u32x4 stq[NCH], sto[NCH];
+  // ---- staging of a block: thread tid holds chunks tid + 512 j of the Q
+  // tile followed by the dO tile, and vector entry tid (kind tid/32: 0 LSE,
+  // 1 Delta, 2 query scale, 3.. P-quant absmax of local group kind-3; query
+  // tid%32).  Loaded into registers one iteration before it is written.
+  u32x4 stg[NCH];
   float stv = 0.0f;
   const int e_kind = tid >> 5, e_q = tid & 31;
   // source row of this thread's vector entry (loop-invariant); entries that
   // are not used read LSE and are discarded, so the load is unconditional
-  // and nothing waits on it before the block is written to LDS
   const int e_grp = grp0 + e_kind - 3;
   const bool e_used = e_kind < 2 || (e_kind == 2 && QKS) || (PQ >= 0 && e_kind >= 3 && e_kind < 3 + NGW && e_grp < a.NG);
   const float* e_src = a.lse + (size_t)bh * Nq;
@@ -548,276 +523,361 @@ __global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
   auto load_stage = [&](int b) __attribute__((always_inline)) {
     const int q0 = qstart(b);
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = tid + 256 * i, row = c / CPR, ch = c % CPR;
+    for (int j = 0; j < NCH; ++j) {
+      const int c = tid + 512 * j, t = c / CHUNKS, within = c % CHUNKS, row = within / CPR, ch = within % CPR;
       const size_t rr = (size_t)min(q0 + row, Nq - 1);
-      stq[i] = *reinterpret_cast<const u32x4*>(qp + rr * D + 8 * ch);
-      sto[i] = *reinterpret_cast<const u32x4*>(dop + rr * D + 8 * ch);
+      stg[j] = *reinterpret_cast<const u32x4*>((t ? dop : qp) + rr * D + 8 * ch);
     }
     stv = e_src[min(q0 + e_q, Nq - 1)];
   };
-  auto write_tiles = [&](int b) __attribute__((always_inline)) {
-    const int slot = b & (DSP_SLOTS - 1);
+  // (slot: compile-time b % DPR_SLOTS, so the LDS addresses fold into offsets)
+  auto write_tiles = [&](auto SLOTc) __attribute__((always_inline)) {
+    constexpr int slot = decltype(SLOTc)::value;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = tid + 256 * i, row = c / CPR, ch = c % CPR;
-      *reinterpret_cast<u32x4*>(q_s[slot] + tile_off<D>(row, ch)) = stq[i];
-      *reinterpret_cast<u32x4*>(do_s[slot] + tile_off<D>(row, ch)) = sto[i];
+    for (int j = 0; j < NCH; ++j) {
+      const int c = tid + 512 * j, t = c / CHUNKS, within = c % CHUNKS, row = within / CPR, ch = within % CPR;
+      *reinterpret_cast<u32x4*>((t ? do_s[slot] : q_s[slot]) + tile_off<D>(row, ch)) = stg[j];
     }
   };
-  auto write_vec = [&](int b) __attribute__((always_inline)) {
-    const int slot = b & (DSP_SLOTS - 1);
+  auto write_vec = [&](int b, auto SLOTc) __attribute__((always_inline)) {
+    constexpr int slot = decltype(SLOTc)::value;
+    const float v = stv;
     const bool ok = e_used && qstart(b) + e_q < Nq;
-    if (e_kind == 0) m_s[slot][e_q] = ok ? stv * LOG2E : 0.0f;
-    else if (e_kind == 1) d_s[slot][e_q] = ok ? stv : 0.0f;
+    // M = +inf for rows past Nq: their p = exp2(S c - M) is exactly 0
+    if (e_kind == 0) m_s[slot][e_q] = ok ? v * LOG2E : INFINITY;
+    else if (e_kind == 1) d_s[slot][e_q] = ok ? v : 0.0f;
     else if (e_kind == 2) {
-      sq_s[slot][e_q] = ok ? stv : 1.0f;
-      // a zero scale (all-zero row) is raised to the smallest normal so that a
-      // masked score stays -inf after the product
-      if constexpr (QKS) cq_s[slot][e_q] = a.c * fmaxf(ok ? stv : 1.0f, 1.17549435e-38f);
-    }
-    else if (PQ >= 0 && e_kind < 3 + NGW) {
-      const FqScale fs = fq_scale<FQF>(ok ? stv : 0.0f);
+      if constexpr (QKS) {
+        sq_s[slot][e_q] = ok ? v : 1.0f;
+        // a zero scale (all-zero row) is raised to the smallest normal so that
+        // a masked score stays -inf after the product
+        cq_s[slot][e_q] = a.c * fmaxf(ok ? v : 1.0f, 1.17549435e-38f);
+      }
+    } else if (PQ >= 0 && e_kind < 3 + NGW) {
+      const FqScale fs = fq_scale<FQF>(ok ? v : 0.0f);
       qs_s[slot][e_kind - 3][e_q] = fs.s;
       qr_s[slot][e_kind - 3][e_q] = fs.r;
     }
   };
 
-  f32x16 acc_dv[NDB], acc_dk[NDB];
+  // prologue: the slots the prologue does not fill (2, 3, and 0, 1 when
+  // the workgroup has fewer blocks) and the P buffers are zeroed: the first
+  // and last iterations' MFMAs read them before or without any block landing
+  // there, so their data must be finite; then blocks 0, 1 in LDS and block 2
+  // in the staging registers
+  {
+    const int z0 = min(NB, 2);   // first slot the prologue leaves empty
+    constexpr int WPS = TILE / 16;   // 16-byte words per slot
+    for (int k = tid; k < 2 * DPR_SLOTS * WPS; k += 512) {
+      const int t = k / (DPR_SLOTS * WPS), sl = (k / WPS) % DPR_SLOTS, o = (k % WPS) * 16;
+      if (sl >= z0) *reinterpret_cast<u32x4*>((t ? do_s[sl] : q_s[sl]) + o) = (u32x4){0u, 0u, 0u, 0u};
+    }
+    f32x4* pz = &p_s[0][0][0][0];
+    for (int k = tid; k < 2 * 4 * 4 * 64; k += 512) pz[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    if (tid < DPR_BQ) {
+      for (int sl = z0; sl < DPR_SLOTS; ++sl) {
+        m_s[sl][tid] = 0.0f;
+        d_s[sl][tid] = 0.0f;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    acc_dv[db] = (f32x16){};
-    acc_dk[db] = (f32x16){};
+        for (int gq = 0; gq < NGW; ++gq) qs_s[sl][gq][tid] = qr_s[sl][gq][tid] = 0.0f;
+        if constexpr (QKS) sq_s[sl][tid] = cq_s[sl][tid] = 0.0f;
+      }
+    }
   }
-  // S/dP of a block (lane: key kj, registers: queries 8(r/4) + 4g + r%4) and
-  // its packed P^ / dS operands (query half h = words 4h .. 4h+3)
-  f32x16 sA, dpA, sB, dpB;
-  uint32_t pA[8], dsA[8], pB[8], dsB[8];
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  if (NB > 0) { load_stage(0); write_tiles(I0{}); write_vec(0, I0{}); }
+  if (NB > 1) { load_stage(1); write_tiles(I1{}); write_vec(1, I1{}); }
+  if (NB > 2) load_stage(2);
 
-  // MFMA step st of iteration b: first the k-steps of S and dP of block b+1,
-  // interleaved (Q or dO row fragment against K or V), so that they are
-  // complete when the next iteration reads them; then st >= NST1: half h,
-  // column block db, {dV, dK} of block b-1 (transposed dO or Q fragment).
-  constexpr int NST1 = NST - NST2;
-  auto fetch = [&](int b, int st_) __attribute__((always_inline)) {
-    const int st = st_ < NST1 ? st_ + NST2 : st_ - NST1;
-    if (st < NST2) {
-      const int h = st / (2 * NDB), r = st % (2 * NDB), db = r >> 1, which = r & 1;
-      const int slot = (b - 1) & (DSP_SLOTS - 1);
-      return lds_tr8<D>(which ? q_s[slot] : do_s[slot], 16 * h, 32 * db, lane);
-    }
-    const int k = st - NST2, ks = k >> 1, which = k & 1;
-    const int slot = (b + 1) & (DSP_SLOTS - 1);
-    return lds_row8<D>(which ? do_s[slot] : q_s[slot], l32, 2 * ks + g);
-  };
-  auto step = [&](const s16x8& frag, int st_, const uint32_t (&Pp)[8], const uint32_t (&DSp)[8], f32x16& S2,
-                  f32x16& DP2) __attribute__((always_inline)) {
-    const int st = st_ < NST1 ? st_ + NST2 : st_ - NST1;
-    if (st < NST2) {
-      const int h = st / (2 * NDB), r = st % (2 * NDB), db = r >> 1, which = r & 1;
-      if (which == 0) {
-        const s16x8 op = __builtin_bit_cast(s16x8, (u32x4){Pp[4 * h], Pp[4 * h + 1], Pp[4 * h + 2], Pp[4 * h + 3]});
-        acc_dv[db] = DT::mfma(frag, op, acc_dv[db]);
-      } else {
-        const s16x8 op = __builtin_bit_cast(s16x8, (u32x4){DSp[4 * h], DSp[4 * h + 1], DSp[4 * h + 2], DSp[4 * h + 3]});
-        acc_dk[db] = DT::mfma(frag, op, acc_dk[db]);
-      }
-    } else {
-      const int k = st - NST2, ks = k >> 1, which = k & 1;
-      if (k == 0) {
-        S2 = (f32x16){};
-        DP2 = (f32x16){};
-      }
-      if (which == 0) S2 = DT::mfma(frag, kf[ks], S2);
-      else DP2 = DT::mfma(frag, vf[ks], DP2);
-    }
-  };
-  // vector work of block b, per quarter u (registers 4u .. 4u+3): read the
-  // per-query vectors, form P, then quantize, form dS and pack both operands.
-  // The reads of a quarter are issued a group or more before their use.
-  float p[16];
-  f32x4 mvv[4], dvv[4], sqv[4], cqv[4], svv[4], rvv[4];
-  auto readvec = [&](int u, int b) __attribute__((always_inline)) {
-    const int slot = b & (DSP_SLOTS - 1), ql = 8 * u + 4 * g;
-    mvv[u] = *reinterpret_cast<const f32x4*>(&m_s[slot][ql]);
-    dvv[u] = *reinterpret_cast<const f32x4*>(&d_s[slot][ql]);
-    sqv[u] = (f32x4){1.0f, 1.0f, 1.0f, 1.0f};
-    if constexpr (QKS) {
-      sqv[u] = *reinterpret_cast<const f32x4*>(&sq_s[slot][ql]);
-      cqv[u] = *reinterpret_cast<const f32x4*>(&cq_s[slot][ql]);
-    }
-    if constexpr (PQ >= 0) {
-      svv[u] = *reinterpret_cast<const f32x4*>(&qs_s[slot][lgrp][ql]);
-      rvv[u] = *reinterpret_cast<const f32x4*>(&qr_s[slot][lgrp][ql]);
-    }
-  };
-  auto form_p = [&](int u, const f32x16& S) __attribute__((always_inline)) {
+  // one wave role for the whole kernel: R = 0 P wave, R = 1 dS wave
+  auto run = [&](auto ROLE) __attribute__((always_inline)) {
+    constexpr int R = decltype(ROLE)::value;
+    // K^T (P wave) or V^T (dS wave) of this wave's 32 keys: lane holds key
+    // kj, d = 16 ks + 8 g .. +7
+    s16x8 kv[NKS];
+    {
+      const bool ok = kj < Nkv;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 4 * u + e;
-      const float sr = QKS ? S[r] * sk_lane : S[r];
-      const float cr = QKS ? cqv[u][e] : a.c;
-      p[r] = fast_exp2(__builtin_fmaf(sr, cr, -mvv[u][e]));
-    }
-  };
-  auto finish = [&](int u, const f32x16& DP, uint32_t (&Pn)[8], uint32_t (&DSn)[8]) __attribute__((always_inline)) {
-    uint32_t w0, w1;
-    if constexpr (PQ >= 0) {   // P^ = FQ(P) per (query, 64-key group)
-      const FqScale f4[4] = {{svv[u][0], rvv[u][0]}, {svv[u][1], rvv[u][1]}, {svv[u][2], rvv[u][2]},
-                             {svv[u][3], rvv[u][3]}};
-      const f32x4 xq = fq_quad<FQF>(&p[4 * u], f4);
-      w0 = DT::pack2(xq[0], xq[1]);
-      w1 = DT::pack2(xq[2], xq[3]);
-    } else {
-      w0 = DT::pack2(p[4 * u], p[4 * u + 1]);
-      w1 = DT::pack2(p[4 * u + 2], p[4 * u + 3]);
-    }
-    float dsv[4];
+      for (int ks = 0; ks < NKS; ++ks) {
+        kv[ks] = (s16x8){};
+        if (!ok) continue;
+        if constexpr (R == 0) {
+          const uint16_t* kp = (const uint16_t*)a.k + (size_t)bh * Nkv * D;
+          kv[ks] = *reinterpret_cast<const s16x8*>(kp + (size_t)kj * D + 16 * ks + 8 * g);
+        } else if constexpr (VFP8) {
+          const uint8_t* vp = (const uint8_t*)a.v + (size_t)bh * Nkv * D;
+          const float* vsc = a.v_scale + (size_t)bh * D + 16 * ks + 8 * g;
+          const u32x2 codes = *reinterpret_cast<const u32x2*>(vp + (size_t)kj * D + 16 * ks + 8 * g);
+          uint32_t wv[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      dsv[e] = p[4 * u + e] * (DP[4 * u + e] - dvv[u][e]);
-      if constexpr (QKS) dsv[e] *= sqv[u][e];   // dK = sm_scale sum_i dS_ij s_q[i] code_q[i]
-    }
-    Pn[2 * u] = w0;
-    Pn[2 * u + 1] = w1;
-    DSn[2 * u] = DT::pack2(dsv[0], dsv[1]);
-    DSn[2 * u + 1] = DT::pack2(dsv[2], dsv[3]);
-  };
-  // slice j of the vector work, placed in fenced group j (NGRP == 8):
-  //   0: read 0 | 1: P 0, read 1 | 2: finish 0, read 2 | 3: P 1
-  //   4: finish 1, read 3 | 5: P 2 | 6: finish 2, P 3 | 7: finish 3
-  auto valu_piece = [&](int j, int b, const f32x16& S, const f32x16& DP, uint32_t (&Pn)[8],
-                        uint32_t (&DSn)[8]) __attribute__((always_inline)) {
-    switch (j) {
-      case 0: readvec(0, b); break;
-      case 1: form_p(0, S); readvec(1, b); break;
-      case 2: finish(0, DP, Pn, DSn); readvec(2, b); break;
-      case 3: form_p(1, S); break;
-      case 4: finish(1, DP, Pn, DSn); readvec(3, b); break;
-      case 5: form_p(2, S); break;
-      case 6: finish(2, DP, Pn, DSn); form_p(3, S); break;
-      default: finish(3, DP, Pn, DSn); break;
-    }
-  };
-
-  // iteration b: S, DP = block b (in), S2, DP2 = block b+1 (out);
-  // Pp, DSp = operands of block b-1 (in), Pn, DSn = operands of block b (out)
-  auto iteration = [&](int b, f32x16& S, f32x16& DP, f32x16& S2, f32x16& DP2, const uint32_t (&Pp)[8],
-                       const uint32_t (&DSp)[8], uint32_t (&Pn)[8], uint32_t (&DSn)[8],
-                       bool sync) __attribute__((always_inline)) {
-    const bool do2 = b >= 1 && active(b - 1);
-    const bool do1 = b + 1 < NB && active(b + 1);
-    const bool dov = b < NB && active(b);
-    const bool full = do2 && do1 && dov;
-    // staging of block b+4 (loaded in iteration b-1) and loads of block b+5:
-    // inside the first fenced groups on the full path, up front otherwise
-    const bool stw = b + 4 < NB, stl = b + 5 < NB;
-    if (!full) {
-      if (stw) {
-        write_tiles(b + 4);
-        write_vec(b + 4);
-      }
-      if (stl) load_stage(b + 5);
-    }
-    if (dov) {   // masked scores -> -inf before the exponent
-      const int q0 = qstart(b);
-      if ((q0 + DSP_BQ > Nq) || (k0w + 32 > Nkv) || (CAUSAL && q0 < k0w + 31)) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int q = q0 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (q >= Nq || kj >= Nkv || (CAUSAL && kj > q)) S[r] = -INFINITY;
+          for (int h = 0; h < 4; ++h) {
+            const f32x2 f = __builtin_amdgcn_cvt_pk_f32_bf8((int)(codes[h >> 1] >> (16 * (h & 1))), false);
+            wv[h] = BF16::pack2(f[0] * vsc[2 * h], f[1] * vsc[2 * h + 1]);
+          }
+          kv[ks] = __builtin_bit_cast(s16x8, (u32x4){wv[0], wv[1], wv[2], wv[3]});
+        } else {
+          const uint16_t* vp = (const uint16_t*)a.v + (size_t)bh * Nkv * D;
+          kv[ks] = *reinterpret_cast<const s16x8*>(vp + (size_t)kj * D + 16 * ks + 8 * g);
         }
       }
     }
-    if (full) {
+    // per-key scale in the exponent; raised to the smallest normal (and 1 for
+    // absent keys) so that a masked score stays -inf after the product
+    const float sk_lane =
+        (QKS && R == 0) ? (kj < Nkv ? fmaxf(a.k_scale[(size_t)bh * Nkv + kj], 1.17549435e-38f) : 1.0f) : 1.0f;
+    // these loads complete here, so that no wait for them lands inside the
+    // loop (where it would also drain the block loads in flight)
+    wait_vmem();
+    __syncthreads();
+
+    f32x16 acc[NDB];   // dV^T (P wave) or dK^T (dS wave): lane key, registers d
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] = (f32x16){};
+    // score buffers: P wave S(i) / S(i+1), dS wave dP(i-1) / dP(i), by parity
+    f32x16 sb[2] = {(f32x16){}, (f32x16){}};
+    uint32_t op[8];   // packed P^ (P wave) or dS (dS wave) of the block: query half h = words 4h .. 4h+3
+#pragma unroll
+    for (int j = 0; j < 8; ++j) op[j] = 0u;
+    // per-query vectors of a register quarter, double-buffered by quarter
+    // parity: P wave M, c s_q (per-token codes), P-quant s and r; dS wave
+    // Delta, s_q (per-token codes) and the quarter's P from LDS
+    f32x4 v0[2], v1[2], v2[2], v3[2];
+
+    // MFMA step st of iteration i: st < NKS the score k-step st (Q or dO row
+    // fragment against the K^T or V^T registers), else the accumulator step
+    // (h, db) (transposed dO or Q fragment against the packed operand).
+    auto tiles = [&](auto SLOTc, const char*& X, const char*& Y) __attribute__((always_inline)) {
+      constexpr int SL = decltype(SLOTc)::value;   // slot of block i
+      if constexpr (R == 0) {
+        X = q_s[(SL + 1) & (DPR_SLOTS - 1)];
+        Y = do_s[SL];
+      } else {
+        X = do_s[SL];
+        Y = q_s[(SL + DPR_SLOTS - 1) & (DPR_SLOTS - 1)];
+      }
+    };
+    auto fetch = [&](const char* X, const char* Y, int st) __attribute__((always_inline)) {
+      if (st < NKS) return lds_row8<D>(X, l32, 2 * st + g);
+      const int k = st - NKS, h = k / NDB, db = k % NDB;
+      return lds_tr8<D>(Y, 16 * h, 32 * db, lane);
+    };
+    auto step = [&](const s16x8& frag, int st, f32x16& SO) __attribute__((always_inline)) {
+      if (st < NKS) {
+        if (st == 0) SO = (f32x16){};
+        SO = DT::mfma(frag, kv[st], SO);
+      } else {
+        const int k = st - NKS, h = k / NDB, db = k % NDB;
+        const s16x8 o = __builtin_bit_cast(s16x8, (u32x4){op[4 * h], op[4 * h + 1], op[4 * h + 2], op[4 * h + 3]});
+        acc[db] = DT::mfma(frag, o, acc[db]);
+      }
+    };
+    // ---- vector work of a register quarter u (registers 4u .. 4u+3: queries
+    // 8u + 4g + 0..3 of the block), its vectors in buffer u & 1
+    auto read_quarter = [&](int u, int slot, int par) __attribute__((always_inline)) {
+      const int ql = 8 * u + 4 * g, bsel = u & 1;
+      if constexpr (R == 0) {
+        v0[bsel] = *reinterpret_cast<const f32x4*>(&m_s[slot][ql]);
+        if constexpr (QKS) v1[bsel] = *reinterpret_cast<const f32x4*>(&cq_s[slot][ql]);
+        if constexpr (PQ >= 0) {
+          v2[bsel] = *reinterpret_cast<const f32x4*>(&qs_s[slot][lgrp][ql]);
+          v3[bsel] = *reinterpret_cast<const f32x4*>(&qr_s[slot][lgrp][ql]);
+        }
+      } else {
+        v0[bsel] = *reinterpret_cast<const f32x4*>(&d_s[slot][ql]);
+        if constexpr (QKS) v1[bsel] = *reinterpret_cast<const f32x4*>(&sq_s[slot][ql]);
+        v2[bsel] = p_s[par][kw][u][lane];   // P of block i-1, written by the P wave
+      }
+    };
+    // P wave: p = exp2(S c - M) in place (S of block i)
+    auto form_p = [&](int u, f32x16& S) __attribute__((always_inline)) {
+      const int bsel = u & 1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * u + e;
+        const float sr = QKS ? S[r] * sk_lane : S[r];
+        const float cr = QKS ? v1[bsel][e] : a.c;
+        S[r] = fast_exp2(__builtin_fmaf(sr, cr, -v0[bsel][e]));
+      }
+    };
+    // P wave: hand P to the dS wave, P^ = FQ(P) per (query, 64-key group) packed
+    auto finish_p = [&](int u, const f32x16& S, int par) __attribute__((always_inline)) {
+      const int bsel = u & 1;
+      p_s[par][kw][u][lane] = (f32x4){S[4 * u], S[4 * u + 1], S[4 * u + 2], S[4 * u + 3]};
+      uint32_t w0, w1;
+      if constexpr (PQ >= 0) {
+        const FqScale f4[4] = {{v2[bsel][0], v3[bsel][0]}, {v2[bsel][1], v3[bsel][1]},
+                               {v2[bsel][2], v3[bsel][2]}, {v2[bsel][3], v3[bsel][3]}};
+        const float x[4] = {S[4 * u], S[4 * u + 1], S[4 * u + 2], S[4 * u + 3]};
+        const f32x4 xq = fq_quad<FQF>(x, f4);
+        w0 = DT::pack2(xq[0], xq[1]);
+        w1 = DT::pack2(xq[2], xq[3]);
+      } else {
+        w0 = DT::pack2(S[4 * u], S[4 * u + 1]);
+        w1 = DT::pack2(S[4 * u + 2], S[4 * u + 3]);
+      }
+      op[2 * u] = w0;
+      op[2 * u + 1] = w1;
+    };
+    // dS wave: dS = P o (dP - Delta) for block i-1
+    auto finish_ds = [&](int u, const f32x16& DP) __attribute__((always_inline)) {
+      const int bsel = u & 1;
+      float dsv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dsv[e] = v2[bsel][e] * (DP[4 * u + e] - v0[bsel][e]);
+        if constexpr (QKS) dsv[e] *= v1[bsel][e];   // dK = sm_scale sum_i dS_ij s_q[i] code_q[i]
+      }
+      op[2 * u] = DT::pack2(dsv[0], dsv[1]);
+      op[2 * u + 1] = DT::pack2(dsv[2], dsv[3]);
+    };
+    // slice j of the vector work, placed after the MFMAs of fenced group j
+    // (the accumulator MFMAs of query half h, groups 4 + 2h and 5 + 2h, find
+    // their operand words written by then); the vectors of a quarter are read
+    // a slice or more before their use
+    auto slice = [&](int j, auto SLOTc, f32x16& CUR, int par) __attribute__((always_inline)) {
+      constexpr int SL = decltype(SLOTc)::value;
+      if constexpr (R == 0) {
+        constexpr int slot = SL;                                       // block i
+        switch (j) {
+          case 0: read_quarter(0, slot, par); read_quarter(1, slot, par); form_p(0, CUR); break;
+          case 1: finish_p(0, CUR, par); form_p(1, CUR); read_quarter(2, slot, par); break;
+          case 2: finish_p(1, CUR, par); read_quarter(3, slot, par); break;
+          case 3: form_p(2, CUR); break;
+          case 4: finish_p(2, CUR, par); form_p(3, CUR); break;
+          case 5: finish_p(3, CUR, par); break;
+          default: break;
+        }
+      } else {
+        constexpr int slot = (SL + DPR_SLOTS - 1) & (DPR_SLOTS - 1);   // block i - 1
+        switch (j) {
+          case 0: read_quarter(0, slot, par); read_quarter(1, slot, par); break;
+          case 1: finish_ds(0, CUR); read_quarter(2, slot, par); break;
+          case 2: finish_ds(1, CUR); read_quarter(3, slot, par); break;
+          case 3: finish_ds(2, CUR); break;
+          case 4: finish_ds(3, CUR); break;
+          default: break;
+        }
+      }
+    };
+    // Masks (P wave, block i).  Query rows past Nq have M = +inf (write_vec),
+    // so their p is exactly 0; key lanes past Nkv are left unmasked (their K^T
+    // registers are zero), since every MFMA output column belongs to one key
+    // and those columns are never stored.  Only the causal diagonal block
+    // needs a per-element mask: register r holds query q0 + 4g + c_r,
+    // c_r = 8(r/4) + r%4, so kj > q compares one per-lane value with a
+    // constant.  It runs unconditionally (a branch around it makes the
+    // register allocator copy S between the two paths); above the diagonal
+    // dq <= -32 masks nothing, below it the block is inactive anyway.
+    auto mask = [&](int i, f32x16& S) __attribute__((always_inline)) {
+      if constexpr (CAUSAL) {
+        int dq = kj - qstart(i) - 4 * g;
+        asm volatile("" : "+v"(dq));   // keeps dq > c from becoming 16 loop-invariant bounds
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = 8 * (r >> 2) + (r & 3);
+          S[r] = dq > c ? -INFINITY : S[r];
+        }
+      }
+    };
+
+    // iteration i; SLOTc = i % DPR_SLOTS at compile time (the loop is
+    // unrolled by DPR_SLOTS), so every LDS address is a per-lane register
+    // plus an immediate offset
+    auto iteration = [&](int i, auto SLOTc) __attribute__((always_inline)) {
+      constexpr int SL = decltype(SLOTc)::value;
+      constexpr int PAR = SL & 1;
+      // P wave: scores S(i+1) into sb[PAR^1], vector work on S(i) in sb[PAR];
+      // dS wave: dP(i) into sb[PAR], vector work on dP(i-1) in sb[PAR^1]
+      f32x16& SO = R == 0 ? sb[PAR ^ 1] : sb[PAR];
+      f32x16& CUR = R == 0 ? sb[PAR] : sb[PAR ^ 1];
+      constexpr int pb = R == 0 ? PAR : PAR ^ 1;   // P buffer written (P wave) / read (dS wave)
+      // the block of the vector work exists for this wave (else its operand
+      // words are zeroed, and the accumulator MFMAs add nothing)
+      const bool ok = R == 0 ? (i < NB && active(i)) : (i >= 1 && active(i - 1));
+      const bool stw = i + 2 < NB, stl = i + 3 < NB;
+      const char *X, *Y;
+      tiles(SLOTc, X, Y);
+      if (R == 0) mask(i, CUR);
+      // Every iteration runs the same instruction stream: at the edges
+      // (before the first block, after the last, blocks outside the causal
+      // range of this wave's keys) the MFMAs work on finite stale or zeroed
+      // LDS data whose results are never used, or on zero operands, so the
+      // accumulators need no branches (which would make the register
+      // allocator copy them between paths).
       s16x8 ring[AHEAD];
 #pragma unroll
-      for (int st = 0; st < AHEAD; ++st) ring[st] = fetch(b, st);
+      for (int st = 0; st < AHEAD; ++st) ring[st] = fetch(X, Y, st);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < NGRP; ++j) {
 #pragma unroll
-        for (int i = 0; i < GSZ; ++i) {
-          const int st = j * GSZ + i;
+        for (int k = 0; k < GSZ; ++k) {
+          const int st = j * GSZ + k;
           const s16x8 cur = ring[st % AHEAD];
-          if (st + AHEAD < NST) ring[st % AHEAD] = fetch(b, st + AHEAD);
-          step(cur, st, Pp, DSp, S2, DP2);
+          if (st + AHEAD < NST) ring[st % AHEAD] = fetch(X, Y, st + AHEAD);
+          step(cur, st, SO);
         }
-        valu_piece(j, b, S, DP, Pn, DSn);
-        if (j == 0 && stw) write_tiles(b + 4);
-        if (j == 1 && stw) write_vec(b + 4);
-        if (j == 2 && stl) load_stage(b + 5);
+        slice(j, SLOTc, CUR, pb);
+        // operand words of an absent block: zero before the accumulator
+        // MFMAs of query half 0 (group 4) and half 1 (group 6) read them
+        if ((j == 2 || j == 5) && !ok) {
+#pragma unroll
+          for (int w4 = 0; w4 < 4; ++w4) op[(j == 2 ? 0 : 4) + w4] = 0u;
+        }
+        if (j == 0 && stw) write_tiles(std::integral_constant<int, (SL + 2) & (DPR_SLOTS - 1)>{});
+        if (j == 1 && stw) write_vec(i + 2, std::integral_constant<int, (SL + 2) & (DPR_SLOTS - 1)>{});
+        if (j == 2 && stl) load_stage(i + 3);
         __builtin_amdgcn_sched_barrier(0);
       }
-    } else {
-      if (do1) {
-#pragma unroll
-        for (int st = 0; st < NST1; ++st) step(fetch(b, st), st, Pp, DSp, S2, DP2);
-      }
-      if (do2) {
-#pragma unroll
-        for (int st = NST1; st < NST; ++st) step(fetch(b, st), st, Pp, DSp, S2, DP2);
-      }
-      if (dov) {
-#pragma unroll
-        for (int j = 0; j < NGRP; ++j) valu_piece(j, b, S, DP, Pn, DSn);
-      }
-    }
-    if (sync) __syncthreads();
-  };
+      __syncthreads();
+    };
 
-  // prologue: blocks 0 .. 3 in LDS, block 4 staged, S/dP of block 0
+    // P wave: S(0) before the first iteration
+    if (R == 0 && NB > 0 && active(0)) {
+      const char* X0 = q_s[0];
 #pragma unroll
-  for (int b0 = 0; b0 < 4; ++b0) {
-    if (NB > b0) {
-      load_stage(b0);
-      write_tiles(b0);
-      write_vec(b0);
+      for (int st = 0; st < NKS; ++st) step(fetch(X0, X0, st), st, sb[0]);
     }
-  }
-  if (NB > 4) load_stage(4);
-  __syncthreads();
-  if (NB > 0 && active(0)) {
-#pragma unroll
-    for (int st = 0; st < NST1; ++st) step(fetch(-1, st), st, pB, dsB, sA, dpA);
-  }
-  for (int b = 0; b <= NB; b += 2) {
-    iteration(b, sA, dpA, sB, dpB, pB, dsB, pA, dsA, b % 3 == 2);
-    if (b + 1 <= NB) iteration(b + 1, sB, dpB, sA, dpA, pA, dsA, pB, dsB, (b + 1) % 3 == 2);
-  }
+    for (int i = 0; i <= NB; i += DPR_SLOTS) {
+      static_assert(DPR_SLOTS == 4, "the loop is unrolled by the slot count");
+      iteration(i, I0{});
+      if (i + 1 <= NB) iteration(i + 1, I1{});
+      if (i + 2 <= NB) iteration(i + 2, std::integral_constant<int, 2>{});
+      if (i + 3 <= NB) iteration(i + 3, std::integral_constant<int, 3>{});
+    }
 
-  if (kj >= Nkv) return;
-  if (nparts > 1) {   // unscaled fp32 partials [slot][dK, dV][key of the block][D]
-    float* pw = a.dkdv_part + (size_t)((unit - a.n_whole) * nparts + part) * 2 * DSP_BN * D;
-    const int kl = w * 32 + l32;
+    // ---- epilogue: the P wave writes dV, the dS wave dK (times sm_scale)
+    if (kj >= Nkv) return;
+    if (nparts > 1) {   // unscaled fp32 partials [slot][dK, dV][key of the block][D]
+      float* pw = a.dkdv_part + (size_t)((unit - a.n_whole) * nparts + part) * 2 * DPR_BN * D +
+                  (R == 0 ? (size_t)DPR_BN * D : 0);
+      const int kl = kw * 32 + l32;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int d = db * 32 + 8 * u + 4 * g;
+          *reinterpret_cast<f32x4*>(pw + (size_t)kl * D + d) =
+              (f32x4){acc[db][4 * u], acc[db][4 * u + 1], acc[db][4 * u + 2], acc[db][4 * u + 3]};
+        }
+      return;
+    }
+    uint16_t* outp = (uint16_t*)(R == 0 ? a.dv : a.dk) + (size_t)bh * Nkv * D;
+    const float scale = R == 0 ? 1.0f : a.sm_scale;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int d = db * 32 + 8 * u + 4 * g;
-        *reinterpret_cast<f32x4*>(pw + (size_t)kl * D + d) =
-            (f32x4){acc_dk[db][4 * u], acc_dk[db][4 * u + 1], acc_dk[db][4 * u + 2], acc_dk[db][4 * u + 3]};
-        *reinterpret_cast<f32x4*>(pw + (size_t)(DSP_BN + kl) * D + d) =
-            (f32x4){acc_dv[db][4 * u], acc_dv[db][4 * u + 1], acc_dv[db][4 * u + 2], acc_dv[db][4 * u + 3]};
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * u + e] * scale;
+        *reinterpret_cast<u32x2*>(outp + (size_t)kj * D + d) = (u32x2){DT::pack2(x[0], x[1]), DT::pack2(x[2], x[3])};
       }
-    return;
-  }
-  uint16_t* dkp = (uint16_t*)a.dk + (size_t)bh * Nkv * D;
-  uint16_t* dvp = (uint16_t*)a.dv + (size_t)bh * Nkv * D;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int d = db * 32 + 8 * u + 4 * g;
-      float x[4], y[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[e] = acc_dk[db][4 * u + e] * a.sm_scale;
-        y[e] = acc_dv[db][4 * u + e];
-      }
-      *reinterpret_cast<u32x2*>(dkp + (size_t)kj * D + d) = (u32x2){DT::pack2(x[0], x[1]), DT::pack2(x[2], x[3])};
-      *reinterpret_cast<u32x2*>(dvp + (size_t)kj * D + d) = (u32x2){DT::pack2(y[0], y[1]), DT::pack2(y[2], y[3])};
-    }
+  };
+  if (w < 4) run(I0{});
+  else run(I1{});
 }
 
 // Sum of the query-range partials of each split key block, in part order
@@ -825,19 +885,19 @@ __global__ __launch_bounds__(256, 1) void dkdv_sp_kernel(BwdArgs a) {
 // t of workgroup (block, z) handles four consecutive d of one key.
 template <class DT, int D>
 __global__ __launch_bounds__(256) void dkdv_merge_kernel(BwdArgs a, int nkb) {
-  constexpr int PER_BLOCK = DSP_BN * D / 4;   // threads per key block
+  constexpr int PER_BLOCK = DPR_BN * D / 4;   // threads per key block
   const int i = blockIdx.y * 256 + threadIdx.x;
   if (i >= PER_BLOCK) return;
   const int kl = i / (D / 4), d = 4 * (i % (D / 4));
   const int unit = a.n_whole + blockIdx.x;
-  const int bh = unit / nkb, key = (unit % nkb) * DSP_BN + kl;
+  const int bh = unit / nkb, key = (unit % nkb) * DPR_BN + kl;
   if (key >= a.Nkv) return;
-  const float* pw = a.dkdv_part + (size_t)blockIdx.x * a.n_split * 2 * DSP_BN * D;
+  const float* pw = a.dkdv_part + (size_t)blockIdx.x * a.n_split * 2 * DPR_BN * D;
   f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
   for (int p = 0; p < a.n_split; ++p) {
-    const float* q = pw + (size_t)p * 2 * DSP_BN * D;
+    const float* q = pw + (size_t)p * 2 * DPR_BN * D;
     sk += *reinterpret_cast<const f32x4*>(q + (size_t)kl * D + d);
-    sv += *reinterpret_cast<const f32x4*>(q + (size_t)(DSP_BN + kl) * D + d);
+    sv += *reinterpret_cast<const f32x4*>(q + (size_t)(DPR_BN + kl) * D + d);
   }
   const size_t o = ((size_t)bh * a.Nkv + key) * D + d;
   *reinterpret_cast<u32x2*>((uint16_t*)a.dk + o) =
@@ -856,7 +916,7 @@ struct DqK {
 template <class DT, int D, bool CAUSAL, int PQ, int IN>
 struct DkvK {
   static void run(dim3 g, const BwdArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((dkdv_sp_kernel<DT, D, CAUSAL, PQ, IN>), g, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((dkdv_pair_kernel<DT, D, CAUSAL, PQ, IN>), g, dim3(512), 0, st, a);
   }
 };
 
@@ -924,9 +984,9 @@ hipError_t launch_bwd_dq(const Shape& s, const Inputs& in, const void* dout, con
 }
 
 size_t dkdv_part_bytes(const Shape& s) {
-  const long long units = (long long)((s.Nkv + DSP_BN - 1) / DSP_BN) * s.B * s.H;
+  const long long units = (long long)((s.Nkv + DPR_BN - 1) / DPR_BN) * s.B * s.H;
   const long long slots = units * DKDV_MAX_SPLIT < DKDV_PART_SLOTS ? units * DKDV_MAX_SPLIT : DKDV_PART_SLOTS;
-  return (size_t)slots * 2 * DSP_BN * s.D * sizeof(float);
+  return (size_t)slots * 2 * DPR_BN * s.D * sizeof(float);
 }
 
 // Tail split: with U key blocks on C compute units, the last rem = U mod C
@@ -937,9 +997,9 @@ size_t dkdv_part_bytes(const Shape& s) {
 // take k = 2 (half a round), 192 take k = 4 (three quarter rounds).  Causal
 // launches already order their blocks longest first and are left whole.
 static void plan_dkdv(const Shape& s, bool causal, int cus, BwdArgs* a) {
-  const int nkb = (s.Nkv + DSP_BN - 1) / DSP_BN;
+  const int nkb = (s.Nkv + DPR_BN - 1) / DPR_BN;
   const int units = nkb * s.B * s.H;
-  const int nqb = (s.Nq + DSP_BQ - 1) / DSP_BQ;
+  const int nqb = (s.Nq + DPR_BQ - 1) / DPR_BQ;
   a->n_whole = units;
   a->n_split = 1;
   if (causal || cus <= 0 || !a->dkdv_part) return;
@@ -961,7 +1021,7 @@ static void plan_dkdv(const Shape& s, bool causal, int cus, BwdArgs* a) {
 
 template <class DT, int D>
 static void launch_merge(const BwdArgs& a, int nkb, int nblocks, hipStream_t st) {
-  dim3 grid((unsigned)nblocks, (unsigned)((DSP_BN * D / 4 + 255) / 256));
+  dim3 grid((unsigned)nblocks, (unsigned)((DPR_BN * D / 4 + 255) / 256));
   hipLaunchKernelGGL((dkdv_merge_kernel<DT, D>), grid, dim3(256), 0, st, a, nkb);
 }
 
@@ -978,7 +1038,7 @@ hipError_t launch_bwd_dkdv(const Shape& s, const Inputs& in, const void* dout, c
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 0;
   plan_dkdv(s, causal, cus, &a);
-  const int nkb = (s.Nkv + DSP_BN - 1) / DSP_BN;
+  const int nkb = (s.Nkv + DPR_BN - 1) / DPR_BN;
   const int units = nkb * s.B * s.H;
   const int split_blocks = units - a.n_whole;
   dim3 grid((unsigned)(a.n_whole + split_blocks * a.n_split));
