@@ -91,6 +91,9 @@ int check_common(const qat_attn_dims* dims, float sm_scale, int causal, uint32_t
   // one workgroup per 128-row tile per (b, h): the launch must fit a 31-bit grid
   const long long tiles = ((long long)(d.Nq > d.Nkv ? d.Nq : d.Nkv) + 127) / 128;
   if ((long long)d.B * d.H > 65535 || tiles * d.B * d.H > 0x7fffffffLL) return QAT_EUNSUPPORTED;
+  // one head's [N, D] tensor must be addressable by 32-bit byte offsets (the
+  // kernels read tiles through buffer descriptors sized to one head)
+  if ((long long)(d.Nq > d.Nkv ? d.Nq : d.Nkv) * d.D * 2 > 0x7fffffffLL) return QAT_EUNSUPPORTED;
   *empty = (d.B == 0 || d.H == 0 || d.Nq == 0);
   if (!*empty && d.Nkv == 0) return QAT_EINVAL;   // softmax over no keys
   return QAT_OK;

@@ -505,58 +505,74 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
   // some (query, key) pair of block b and this wave's keys is unmasked
   auto active = [&](int b) { return wave_live && (!CAUSAL || qstart(b) + DPR_BQ - 1 >= k0w); };
 
-  // ---- staging of a block: thread tid holds chunks tid + 512 j of the Q
-  // tile followed by the dO tile, and vector entry tid (kind tid/32: 0 LSE,
-  // 1 Delta, 2 query scale, 3.. P-quant absmax of local group kind-3; query
-  // tid%32).  Loaded into registers one iteration before it is written.
+  // ---- staging of a block, loaded into registers one iteration before it
+  // is written to LDS.  Q and dO tiles: thread tid holds chunks tid + 512 j
+  // (the Q tile, then the dO tile), read with buffer loads whose range is the
+  // head's Nq rows, so rows past Nq read as zeros and each address is a fixed
+  // per-thread offset plus the block's uniform row offset.  Per-query
+  // vectors, one wave each so that control flow stays uniform: wave 0 LSE
+  // (lanes 0-31) and Delta (lanes 32-63), wave 1 the P-quant absmax of the
+  // workgroup's two 64-key groups (group lane / 32), wave 2 the per-token
+  // query scale (per-token codes only).
   u32x4 stg[NCH];
   float stv = 0.0f;
-  const int e_kind = tid >> 5, e_q = tid & 31;
-  // source row of this thread's vector entry (loop-invariant); entries that
-  // are not used read LSE and are discarded, so the load is unconditional
-  const int e_grp = grp0 + e_kind - 3;
-  const bool e_used = e_kind < 2 || (e_kind == 2 && QKS) || (PQ >= 0 && e_kind >= 3 && e_kind < 3 + NGW && e_grp < a.NG);
-  const float* e_src = a.lse + (size_t)bh * Nq;
-  if (e_used && e_kind == 1) e_src = a.delta + (size_t)bh * Nq;
-  if (e_used && e_kind == 2) e_src = a.q_scale + (size_t)bh * Nq;
-  if (e_used && e_kind >= 3) e_src = a.p_amax_in + ((size_t)bh * a.NG + e_grp) * Nq;
+  const __amdgpu_buffer_rsrc_t rsrc_q = __builtin_amdgcn_make_buffer_rsrc((void*)qp, 0, Nq * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsrc_do = __builtin_amdgcn_make_buffer_rsrc((void*)dop, 0, Nq * D * 2, 0x00020000);
+  // tensor of chunk j: with D = 128 chunk j of every thread is tensor j; with
+  // D = 64 waves 0-3 hold the Q tile and waves 4-7 the dO tile
+  auto st_tensor = [&](int j) { return CHUNKS == 512 ? j == 1 : w >= 4; };
+  auto st_within = [&](int j) { return (tid + 512 * j) % CHUNKS; };
+  const float* v_src = nullptr;   // wave 0-2: this lane's vector source (per head), else unused
+  bool v_live = false;            // the lane's vector entry exists (wave 1: group inside the keys)
+  if (w == 0) {
+    v_src = (lane < 32 ? a.lse : a.delta) + (size_t)bh * Nq;
+    v_live = true;
+  } else if (w == 1 && PQ >= 0) {
+    const int gq = grp0 + g;
+    v_live = g < NGW && gq < a.NG;
+    v_src = a.p_amax_in + ((size_t)bh * a.NG + (v_live ? gq : 0)) * Nq;
+  } else if (w == 2 && QKS && lane < 32) {
+    v_src = a.q_scale + (size_t)bh * Nq;
+    v_live = true;
+  }
   auto load_stage = [&](int b) __attribute__((always_inline)) {
     const int q0 = qstart(b);
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int c = tid + 512 * j, t = c / CHUNKS, within = c % CHUNKS, row = within / CPR, ch = within % CPR;
-      const size_t rr = (size_t)min(q0 + row, Nq - 1);
-      stg[j] = *reinterpret_cast<const u32x4*>((t ? dop : qp) + rr * D + 8 * ch);
+      const int within = st_within(j), row = within / CPR, ch = within % CPR;
+      stg[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            st_tensor(j) ? rsrc_do : rsrc_q, row * D * 2 + ch * 16, q0 * D * 2, 0));
     }
-    stv = e_src[min(q0 + e_q, Nq - 1)];
+    if (w < 3 && v_live) stv = v_src[min(q0 + l32, Nq - 1)];
   };
   // (slot: compile-time b % DPR_SLOTS, so the LDS addresses fold into offsets)
   auto write_tiles = [&](auto SLOTc) __attribute__((always_inline)) {
     constexpr int slot = decltype(SLOTc)::value;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int c = tid + 512 * j, t = c / CHUNKS, within = c % CHUNKS, row = within / CPR, ch = within % CPR;
-      *reinterpret_cast<u32x4*>((t ? do_s[slot] : q_s[slot]) + tile_off<D>(row, ch)) = stg[j];
+      const int within = st_within(j), row = within / CPR, ch = within % CPR;
+      *reinterpret_cast<u32x4*>((st_tensor(j) ? do_s[slot] : q_s[slot]) + tile_off<D>(row, ch)) = stg[j];
     }
   };
   auto write_vec = [&](int b, auto SLOTc) __attribute__((always_inline)) {
     constexpr int slot = decltype(SLOTc)::value;
     const float v = stv;
-    const bool ok = e_used && qstart(b) + e_q < Nq;
-    // M = +inf for rows past Nq: their p = exp2(S c - M) is exactly 0
-    if (e_kind == 0) m_s[slot][e_q] = ok ? v * LOG2E : INFINITY;
-    else if (e_kind == 1) d_s[slot][e_q] = ok ? v : 0.0f;
-    else if (e_kind == 2) {
-      if constexpr (QKS) {
-        sq_s[slot][e_q] = ok ? v : 1.0f;
-        // a zero scale (all-zero row) is raised to the smallest normal so that
-        // a masked score stays -inf after the product
-        cq_s[slot][e_q] = a.c * fmaxf(ok ? v : 1.0f, 1.17549435e-38f);
-      }
-    } else if (PQ >= 0 && e_kind < 3 + NGW) {
+    const bool ok = v_live && qstart(b) + l32 < Nq;
+    if (w == 0) {
+      // M = +inf for rows past Nq: their p = exp2(S c - M) is exactly 0
+      float* dst = lane < 32 ? &m_s[slot][l32] : &d_s[slot][l32];
+      *dst = lane < 32 ? (ok ? v * LOG2E : INFINITY) : (ok ? v : 0.0f);
+    } else if (w == 1 && PQ >= 0) {
       const FqScale fs = fq_scale<FQF>(ok ? v : 0.0f);
-      qs_s[slot][e_kind - 3][e_q] = fs.s;
-      qr_s[slot][e_kind - 3][e_q] = fs.r;
+      if (g < NGW) {
+        qs_s[slot][g][l32] = fs.s;
+        qr_s[slot][g][l32] = fs.r;
+      }
+    } else if (w == 2 && QKS && lane < 32) {
+      sq_s[slot][l32] = ok ? v : 1.0f;
+      // a zero scale (all-zero row) is raised to the smallest normal so that
+      // a masked score stays -inf after the product
+      cq_s[slot][l32] = a.c * fmaxf(ok ? v : 1.0f, 1.17549435e-38f);
     }
   };
 
