@@ -156,6 +156,21 @@ __device__ __forceinline__ float row_delta(const s16x8 (&ohf)[D / 16], const s16
   }
 }
 
+
+// Power-of-two scale for a row of fp16 MFMA operands whose absolute maximum
+// is m: x * up lands the largest at [2^14, 2^15) (every fp16 keeps 11
+// significant bits down to 2^-10 of that maximum), and down = 1 / up undoes
+// it on the fp32 product.  Both exact; m == 0 gives up = down = 1.
+struct Pow2Scale { float up, down; };
+__device__ __forceinline__ Pow2Scale pow2_scale(float m) {
+  int e = (int)((__builtin_bit_cast(uint32_t, m) >> 23) & 0xFF) - 127;   // exponent of m (m >= 0)
+  e = m > 0.0f ? min(max(e, -100), 100) : 14;
+  Pow2Scale r;
+  r.up = __builtin_bit_cast(float, (uint32_t)(127 + 14 - e) << 23);
+  r.down = __builtin_bit_cast(float, (uint32_t)(127 - 14 + e) << 23);
+  return r;
+}
+
 constexpr int DQ_BM = 128;
 constexpr int DQ_BN = 64;
 
@@ -210,18 +225,33 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   } else {
     Di = qi < Nq ? a.delta[(size_t)bh * Nq + qi] : 0.0f;
   }
-  if constexpr (VFP8) {   // dP = (dO * v_scale) code^T: the per-channel V scale moves onto dO
+  // fp8 V: dP = (dO * v_scale) code^T on the fp16 MFMA.  The per-channel V
+  // scale moves onto dO, the row is scaled by a power of two (its largest
+  // product near 2^14) and rounded to fp16 (11 significant bits), and the
+  // codes are exact fp16 values; dp_down undoes the row scale on the result.
+  float dp_down = 1.0f;
+  if constexpr (VFP8) {
+    float prod[NKS][8];
+    float mx = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const f32x4 s0 = *reinterpret_cast<const f32x4*>(vsc + 16 * ks + 8 * g);
       const f32x4 s1 = *reinterpret_cast<const f32x4*>(vsc + 16 * ks + 8 * g + 4);
       const float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
       const u32x4 wd = __builtin_bit_cast(u32x4, dof[ks]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        prod[ks][e] = BF16::to_f32((uint16_t)(wd[e >> 1] >> (16 * (e & 1)))) * sc[e];
+        mx = fmaxf(mx, fabsf(prod[ks][e]));
+      }
+    }
+    const Pow2Scale ps = pow2_scale(max_xor32(mx));
+    dp_down = ps.down;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
       u32x4 ws;
 #pragma unroll
-      for (int h = 0; h < 4; ++h)
-        ws[h] = BF16::pack2(BF16::to_f32((uint16_t)(wd[h] & 0xFFFFu)) * sc[2 * h],
-                            BF16::to_f32((uint16_t)(wd[h] >> 16)) * sc[2 * h + 1]);
+      for (int h = 0; h < 4; ++h) ws[h] = FP16::pack2(prod[ks][2 * h] * ps.up, prod[ks][2 * h + 1] * ps.up);
       dof[ks] = __builtin_bit_cast(s16x8, ws);
     }
   }
@@ -264,21 +294,15 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
     }
   };
   auto finish_tile = [&](int buf) {
-    if constexpr (VFP8) {   // the code values themselves (exact in bf16); v_scale is on dO
+    if constexpr (VFP8) {   // the code values themselves as fp16 (exact: an e5m2 code is an fp16's high byte)
 #pragma unroll
       for (int u = 0; u < VC_PER_THREAD; ++u) {
         const int P = (u * 4 + w) * 1024 + lane * 16, row = P / D, c0 = P % D;
         const u32x4 codes = *reinterpret_cast<const u32x4*>(vc_s + P);
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {   // 8 codes -> one 16-byte chunk of the bf16 tile
-          u32x4 vv;
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            const f32x2 f = __builtin_amdgcn_cvt_pk_f32_bf8((int)(codes[2 * h2 + (h >> 1)] >> (16 * (h & 1))), false);
-            vv[h] = BF16::pack2(f[0], f[1]);
-          }
-          *reinterpret_cast<u32x4*>(smem[buf][1] + tile_off<D>(row, c0 / 8 + h2)) = vv;
-        }
+        for (int h2 = 0; h2 < 2; ++h2)   // 8 codes -> one 16-byte chunk of the fp16 tile
+          *reinterpret_cast<s16x8*>(smem[buf][1] + tile_off<D>(row, c0 / 8 + h2)) =
+              e5m2x8_to_f16((int)codes[2 * h2], (int)codes[2 * h2 + 1]);
       }
     }
     if constexpr (QKS) {
@@ -309,7 +333,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         s[kb] = DT::mfma(lds_row8<D>(Kt, kb * 32 + l32, 2 * ks + g), qf[ks], s[kb]);
-        dp[kb] = DT::mfma(lds_row8<D>(Vt, kb * 32 + l32, 2 * ks + g), dof[ks], dp[kb]);
+        if constexpr (VFP8) dp[kb] = FP16::mfma(lds_row8<D>(Vt, kb * 32 + l32, 2 * ks + g), dof[ks], dp[kb]);
+        else dp[kb] = DT::mfma(lds_row8<D>(Vt, kb * 32 + l32, 2 * ks + g), dof[ks], dp[kb]);
       }
     }
     const bool need_mask = (kv0 + DQ_BN > Nkv) || (CAUSAL && kv0 + DQ_BN - 1 > q0);
@@ -356,7 +381,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ds_rowsum += p[kb][r] * (dp[kb][r] - Di);
+        for (int r = 0; r < 16; ++r) ds_rowsum += p[kb][r] * __builtin_fmaf(dp[kb][r], dp_down, -Di);
     }
     // dQ^T += K^T dS^T
 #pragma unroll
@@ -366,7 +391,14 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int r0 = 8 * h + 2 * jj;
-        float d0 = p[kb][r0] * (dp[kb][r0] - Di), d1 = p[kb][r0 + 1] * (dp[kb][r0 + 1] - Di);
+        float d0, d1;
+        if constexpr (VFP8) {
+          d0 = p[kb][r0] * __builtin_fmaf(dp[kb][r0], dp_down, -Di);
+          d1 = p[kb][r0 + 1] * __builtin_fmaf(dp[kb][r0 + 1], dp_down, -Di);
+        } else {
+          d0 = p[kb][r0] * (dp[kb][r0] - Di);
+          d1 = p[kb][r0 + 1] * (dp[kb][r0 + 1] - Di);
+        }
         if constexpr (QKS) {   // dQ = sm_scale sum_j dS_ij s_k[j] code_k[j]
           const f32x2 k2 = *reinterpret_cast<const f32x2*>(&ks_s[buf][kb * 32 + 8 * (r0 >> 2) + 4 * g + (r0 & 3)]);
           d0 *= k2[0];
@@ -435,6 +467,24 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 // written in iteration i was last read in iteration i-1, before the barrier;
 // the P buffer of parity i&1 is rewritten in iteration i+2, after the
 // barrier that ends the dS wave's read of it in iteration i+1.
+// Maximum over aligned groups of N consecutive lanes (N = 8 or 16) by DPP:
+// the partner exchanges lane ^ 1, lane ^ 2, the mirror within eight lanes and
+// (N = 16) the mirror within sixteen leave every lane with its group's max.
+template <int N>
+__device__ __forceinline__ float row_max_dpp(float x) {
+  static_assert(N == 8 || N == 16, "group");
+  auto step = [](float v, auto CTRL) {
+    constexpr int c = decltype(CTRL)::value;
+    const int o = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), c, 0xF, 0xF, false);
+    return fmaxf(v, __builtin_bit_cast(float, o));
+  };
+  x = step(x, std::integral_constant<int, 0xB1>{});    // quad_perm [1,0,3,2]
+  x = step(x, std::integral_constant<int, 0x4E>{});    // quad_perm [2,3,0,1]
+  x = step(x, std::integral_constant<int, 0x141>{});   // row_half_mirror
+  if constexpr (N == 16) x = step(x, std::integral_constant<int, 0x140>{});   // row_mirror
+  return x;
+}
+
 constexpr int DPR_BN = 128;    // keys per workgroup
 constexpr int DPR_BQ = 32;     // queries per block
 constexpr int DPR_SLOTS = 4;   // LDS slots of Q/dO blocks
@@ -465,6 +515,12 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float qs_s[DPR_SLOTS][NGW][DPR_BQ];
   __shared__ __attribute__((aligned(16))) float qr_s[DPR_SLOTS][NGW][DPR_BQ];
   __shared__ __attribute__((aligned(16))) f32x4 p_s[2][4][4][64];   // [block parity][key quarter][reg quarter][lane]
+  // fp8 V: dO * v_scale rows scaled by a power of two and rounded to fp16 (the
+  // dS wave's dP operand; dV keeps the plain dO tile), and each row's inverse
+  // scale
+  __shared__ __attribute__((aligned(16))) char dos_s[VFP8 ? DPR_SLOTS : 1][VFP8 ? TILE : 16];
+  __shared__ __attribute__((aligned(16))) float es_s[VFP8 ? DPR_SLOTS : 1][DPR_BQ];
+  __shared__ __attribute__((aligned(16))) float vs_s[VFP8 ? D : 1];
 
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int kw = w & 3;   // this wave's 32 keys within the workgroup
@@ -522,6 +578,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
   // D = 64 waves 0-3 hold the Q tile and waves 4-7 the dO tile
   auto st_tensor = [&](int j) { return CHUNKS == 512 ? j == 1 : w >= 4; };
   auto st_within = [&](int j) { return (tid + 512 * j) % CHUNKS; };
+  if constexpr (VFP8) {   // fp8 V: the head's v_scale in LDS (read where the dO copy is scaled)
+    if (tid < D) vs_s[tid] = a.v_scale[(size_t)bh * D + tid];
+    __syncthreads();
+  }
   const float* v_src = nullptr;   // wave 0-2: this lane's vector source (per head), else unused
   bool v_live = false;            // the lane's vector entry exists (wave 1: group inside the keys)
   if (w == 0) {
@@ -552,6 +612,26 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
     for (int j = 0; j < NCH; ++j) {
       const int within = st_within(j), row = within / CPR, ch = within % CPR;
       *reinterpret_cast<u32x4*>((st_tensor(j) ? do_s[slot] : q_s[slot]) + tile_off<D>(row, ch)) = stg[j];
+      if constexpr (VFP8) {
+        if (st_tensor(j)) {   // the row's CPR chunks sit in CPR consecutive lanes
+          const f32x4 va = *reinterpret_cast<const f32x4*>(&vs_s[8 * ch]);
+          const f32x4 vb = *reinterpret_cast<const f32x4*>(&vs_s[8 * ch + 4]);
+          const float vs8[8] = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+          float x[8], m = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            x[e] = BF16::to_f32((uint16_t)(stg[j][e >> 1] >> (16 * (e & 1)))) * vs8[e];
+            m = fmaxf(m, fabsf(x[e]));
+          }
+          m = row_max_dpp<CPR>(m);
+          const Pow2Scale ps = pow2_scale(m);
+          u32x4 h;
+#pragma unroll
+          for (int k2 = 0; k2 < 4; ++k2) h[k2] = FP16::pack2(x[2 * k2] * ps.up, x[2 * k2 + 1] * ps.up);
+          *reinterpret_cast<u32x4*>(dos_s[slot] + tile_off<D>(row, ch)) = h;
+          if (ch == 0) es_s[slot][row] = ps.down;
+        }
+      }
     }
   };
   auto write_vec = [&](int b, auto SLOTc) __attribute__((always_inline)) {
@@ -587,6 +667,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
     for (int k = tid; k < 2 * DPR_SLOTS * WPS; k += 512) {
       const int t = k / (DPR_SLOTS * WPS), sl = (k / WPS) % DPR_SLOTS, o = (k % WPS) * 16;
       if (sl >= z0) *reinterpret_cast<u32x4*>((t ? do_s[sl] : q_s[sl]) + o) = (u32x4){0u, 0u, 0u, 0u};
+      if constexpr (VFP8) {
+        if (sl >= z0 && t) *reinterpret_cast<u32x4*>(dos_s[VFP8 ? sl : 0] + o) = (u32x4){0u, 0u, 0u, 0u};
+      }
     }
     f32x4* pz = &p_s[0][0][0][0];
     for (int k = tid; k < 2 * 4 * 4 * 64; k += 512) pz[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -597,6 +680,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
         for (int gq = 0; gq < NGW; ++gq) qs_s[sl][gq][tid] = qr_s[sl][gq][tid] = 0.0f;
         if constexpr (QKS) sq_s[sl][tid] = cq_s[sl][tid] = 0.0f;
+        if constexpr (VFP8) es_s[VFP8 ? sl : 0][tid] = 0.0f;
       }
     }
   }
@@ -621,17 +705,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
         if constexpr (R == 0) {
           const uint16_t* kp = (const uint16_t*)a.k + (size_t)bh * Nkv * D;
           kv[ks] = *reinterpret_cast<const s16x8*>(kp + (size_t)kj * D + 16 * ks + 8 * g);
-        } else if constexpr (VFP8) {
+        } else if constexpr (VFP8) {   // the e5m2 codes as fp16 values (exact); v_scale is on dO
           const uint8_t* vp = (const uint8_t*)a.v + (size_t)bh * Nkv * D;
-          const float* vsc = a.v_scale + (size_t)bh * D + 16 * ks + 8 * g;
           const u32x2 codes = *reinterpret_cast<const u32x2*>(vp + (size_t)kj * D + 16 * ks + 8 * g);
-          uint32_t wv[4];
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            const f32x2 f = __builtin_amdgcn_cvt_pk_f32_bf8((int)(codes[h >> 1] >> (16 * (h & 1))), false);
-            wv[h] = BF16::pack2(f[0] * vsc[2 * h], f[1] * vsc[2 * h + 1]);
-          }
-          kv[ks] = __builtin_bit_cast(s16x8, (u32x4){wv[0], wv[1], wv[2], wv[3]});
+          kv[ks] = e5m2x8_to_f16((int)codes[0], (int)codes[1]);
         } else {
           const uint16_t* vp = (const uint16_t*)a.v + (size_t)bh * Nkv * D;
           kv[ks] = *reinterpret_cast<const s16x8*>(vp + (size_t)kj * D + 16 * ks + 8 * g);
@@ -669,7 +746,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
         X = q_s[(SL + 1) & (DPR_SLOTS - 1)];
         Y = do_s[SL];
       } else {
-        X = do_s[SL];
+        X = VFP8 ? dos_s[VFP8 ? SL : 0] : do_s[SL];
         Y = q_s[(SL + DPR_SLOTS - 1) & (DPR_SLOTS - 1)];
       }
     };
@@ -681,7 +758,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
     auto step = [&](const s16x8& frag, int st, f32x16& SO) __attribute__((always_inline)) {
       if (st < NKS) {
         if (st == 0) SO = (f32x16){};
-        SO = DT::mfma(frag, kv[st], SO);
+        if constexpr (VFP8 && R == 1) SO = FP16::mfma(frag, kv[st], SO);
+        else SO = DT::mfma(frag, kv[st], SO);
       } else {
         const int k = st - NKS, h = k / NDB, db = k % NDB;
         const s16x8 o = __builtin_bit_cast(s16x8, (u32x4){op[4 * h], op[4 * h + 1], op[4 * h + 2], op[4 * h + 3]});
@@ -702,6 +780,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
       } else {
         v0[bsel] = *reinterpret_cast<const f32x4*>(&d_s[slot][ql]);
         if constexpr (QKS) v1[bsel] = *reinterpret_cast<const f32x4*>(&sq_s[slot][ql]);
+        if constexpr (VFP8) v1[bsel] = *reinterpret_cast<const f32x4*>(&es_s[VFP8 ? slot : 0][ql]);
         v2[bsel] = p_s[par][kw][u][lane];   // P of block i-1, written by the P wave
       }
     };
@@ -741,7 +820,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
       float dsv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        dsv[e] = v2[bsel][e] * (DP[4 * u + e] - v0[bsel][e]);
+        if constexpr (VFP8) dsv[e] = v2[bsel][e] * __builtin_fmaf(DP[4 * u + e], v1[bsel][e], -v0[bsel][e]);
+        else dsv[e] = v2[bsel][e] * (DP[4 * u + e] - v0[bsel][e]);
         if constexpr (QKS) dsv[e] *= v1[bsel][e];   // dK = sm_scale sum_i dS_ij s_q[i] code_q[i]
       }
       op[2 * u] = DT::pack2(dsv[0], dsv[1]);
