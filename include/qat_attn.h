@@ -53,6 +53,7 @@ extern "C" {
 #define QAT_EUNSUPPORTED 2  /* valid request the library does not implement   */
 #define QAT_EWORKSPACE 3    /* workspace pointer null or smaller than needed  */
 #define QAT_EHIP 4          /* a kernel launch failed                         */
+#define QAT_ESCRATCH 5      /* qat_attn_bwd_noalloc: beyond its static scratch */
 
 /* storage dtypes */
 #define QAT_DTYPE_BF16 0
@@ -162,6 +163,31 @@ int qat_attn_bwd_stages(const qat_attn_dims* dims, const void* q, const void* k,
                         float sm_scale, int causal, uint32_t quant_flags,
                         void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                         uint32_t stages, void* stream);
+
+/*
+ * The backward without allocation and without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Arguments, results
+ * and errors are those of qat_attn_bwd, except that:
+ *  - its scratch is a static device array of QAT_NOALLOC_SCRATCH_BYTES that
+ *    the library holds on every GPU it runs on until the process ends (its
+ *    address is looked up on the first call on each device); the call
+ *    allocates nothing and needs none of its contents to start at zero;
+ *  - problems whose scratch exceeds that size (qat_attn_workspace_bytes(dims,
+ *    flags, 1) less the dK/dV partial sums) return QAT_ESCRATCH with nothing
+ *    enqueued: e.g. the DiT image shape (B1 H24 N4608 D128, 33 MB) fits,
+ *    per-token Q/K/V quantization at long-video size does not;
+ *  - every dK/dV key block runs whole (no query-range split), so dK and dV
+ *    may differ from qat_attn_bwd's in the last bits (fp32 summation order);
+ *  - all calls on one GPU share its scratch: calls that overlap on one GPU
+ *    (other streams, other host threads) race and must be serialised by the
+ *    caller.
+ */
+#define QAT_NOALLOC_SCRATCH_BYTES (64u << 20)
+int qat_attn_bwd_noalloc(const qat_attn_dims* dims, const void* q, const void* k, const void* v,
+                         const float* v_scale, const void* o_hp, const float* lse, const void* dout,
+                         float sm_scale, int causal, uint32_t quant_flags,
+                         void* dq, void* dk, void* dv, void* stream);
 
 /*
  * Chunked-KV mode on one GPU: the local half of ring attention ("usp:

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 OUT = os.path.join(HERE, "libqat_attn.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "quant.hip", "merge.hip", "api.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "quant.hip", "merge.hip", "api.cpp", "noalloc.hip"]
 ARCH = "gfx950"
 
 

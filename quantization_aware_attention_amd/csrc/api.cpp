@@ -9,6 +9,7 @@
 #include <cstdint>
 
 #include "launch.hpp"
+#include "api_internal.hpp"
 
 namespace {
 
@@ -32,7 +33,9 @@ struct Layout {
   size_t delta = 0, amax = 0, part = 0, kpart = 0, kmean = 0, ksm = 0, qh = 0, kh = 0, vh = 0, qs = 0, ks = 0, total = 0;
 };
 
-Layout layout(const qat_attn_dims& d, uint32_t flags, int pass) {
+// with_partials = false leaves out the dK/dV tail-split partial sums (the
+// backward then runs every key block whole)
+Layout layout(const qat_attn_dims& d, uint32_t flags, int pass, bool with_partials = true) {
   Layout L;
   const size_t BH = (size_t)d.B * d.H;
   size_t off = 0;
@@ -45,7 +48,7 @@ Layout layout(const qat_attn_dims& d, uint32_t flags, int pass) {
       off += align_up(BH * ng * d.Nq * sizeof(float));
     }
     L.part = off;
-    off += align_up(qat::dkdv_part_bytes(shape_of(d)));
+    if (with_partials) off += align_up(qat::dkdv_part_bytes(shape_of(d)));
   }
   if (flags & QAT_SMOOTH_K) {
     L.kpart = off;
@@ -156,6 +159,56 @@ qat::Inputs prepared_inputs(const Layout& L, uint32_t flags, const void* q, cons
 
 }  // namespace
 
+size_t qat::bwd_bytes_whole(const qat_attn_dims* dims, uint32_t quant_flags) {
+  if (!dims) return 0;
+  const qat_attn_dims& d = *dims;
+  if (d.B < 0 || d.H < 0 || d.Nq < 0 || d.Nkv < 0 || d.D <= 0) return 0;
+  return layout(d, quant_flags, 1, false).total;
+}
+
+int qat::bwd_impl(const qat_attn_dims* dims, const void* q, const void* k, const void* v,
+                  const float* v_scale, const void* o_hp, const float* lse, const void* dout,
+                  float sm_scale, int causal, uint32_t quant_flags,
+                  void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                  uint32_t stages, bool split_tail, void* stream) {
+  if (stages == 0 || (stages & ~QAT_BWD_ALL)) return QAT_EINVAL;
+  bool empty = false;
+  int rc = check_common(dims, sm_scale, causal, quant_flags, v_scale, &empty);
+  if (rc != QAT_OK) return rc;
+  if (empty) return QAT_OK;
+  const void* need[] = {q, k, v, o_hp, lse, dout, dq, dk, dv};
+  for (const void* p : need)
+    if ((rc = check_ptr(p)) != QAT_OK) return rc;
+  if (v_scale && !aligned16(v_scale)) return QAT_EINVAL;
+  const qat_attn_dims& d = *dims;
+  const Layout L = layout(d, quant_flags, 1, split_tail);
+  if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return QAT_EWORKSPACE;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const qat::Shape s = shape_of(d);
+  char* ws = static_cast<char*>(workspace);
+  qat::Inputs in;
+  if (stages & QAT_BWD_PREPARE) {
+    if ((rc = prepare_inputs(d, L, quant_flags, q, k, v, v_scale, ws, st, &in)) != QAT_OK) return rc;
+  } else {   // later stages read what the prepare stage left in the workspace
+    in = prepared_inputs(L, quant_flags, q, k, v, v_scale, ws);
+  }
+  float* delta = reinterpret_cast<float*>(ws + L.delta);
+  float* amax = (quant_flags & QAT_P_QUANT) ? reinterpret_cast<float*>(ws + L.amax) : nullptr;
+  const int pfmt = pfmt_of(quant_flags);
+  // Delta together with dQ: the dQ kernel forms it for its rows (bit for bit
+  // as the separate pass) and publishes it for dK/dV, one launch fewer
+  const bool delta_in_dq = (stages & QAT_BWD_DELTA) && (stages & QAT_BWD_DQ);
+  if ((stages & QAT_BWD_DELTA) && !delta_in_dq) QAT_TRY(qat::launch_bwd_delta(s, o_hp, dout, delta, st));
+  if (stages & QAT_BWD_DQ)
+    QAT_TRY(qat::launch_bwd_dq(s, in, dout, lse, delta, delta_in_dq ? o_hp : nullptr, sm_scale, causal != 0, pfmt,
+                               dq, amax, st));
+  if (stages & QAT_BWD_DKDV)
+    QAT_TRY(qat::launch_bwd_dkdv(s, in, dout, lse, delta, amax, sm_scale, causal != 0, pfmt, dk, dv,
+                                 split_tail ? reinterpret_cast<float*>(ws + L.part) : nullptr, st));
+  return QAT_OK;
+}
+
 extern "C" {
 
 size_t qat_attn_workspace_bytes(const qat_attn_dims* dims, uint32_t quant_flags, int pass) {
@@ -195,42 +248,8 @@ int qat_attn_bwd_stages(const qat_attn_dims* dims, const void* q, const void* k,
                         float sm_scale, int causal, uint32_t quant_flags,
                         void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                         uint32_t stages, void* stream) {
-  if (stages == 0 || (stages & ~QAT_BWD_ALL)) return QAT_EINVAL;
-  bool empty = false;
-  int rc = check_common(dims, sm_scale, causal, quant_flags, v_scale, &empty);
-  if (rc != QAT_OK) return rc;
-  if (empty) return QAT_OK;
-  const void* need[] = {q, k, v, o_hp, lse, dout, dq, dk, dv};
-  for (const void* p : need)
-    if ((rc = check_ptr(p)) != QAT_OK) return rc;
-  if (v_scale && !aligned16(v_scale)) return QAT_EINVAL;
-  const qat_attn_dims& d = *dims;
-  const Layout L = layout(d, quant_flags, 1);
-  if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return QAT_EWORKSPACE;
-
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const qat::Shape s = shape_of(d);
-  char* ws = static_cast<char*>(workspace);
-  qat::Inputs in;
-  if (stages & QAT_BWD_PREPARE) {
-    if ((rc = prepare_inputs(d, L, quant_flags, q, k, v, v_scale, ws, st, &in)) != QAT_OK) return rc;
-  } else {   // later stages read what the prepare stage left in the workspace
-    in = prepared_inputs(L, quant_flags, q, k, v, v_scale, ws);
-  }
-  float* delta = reinterpret_cast<float*>(ws + L.delta);
-  float* amax = (quant_flags & QAT_P_QUANT) ? reinterpret_cast<float*>(ws + L.amax) : nullptr;
-  const int pfmt = pfmt_of(quant_flags);
-  // Delta together with dQ: the dQ kernel forms it for its rows (bit for bit
-  // as the separate pass) and publishes it for dK/dV, one launch fewer
-  const bool delta_in_dq = (stages & QAT_BWD_DELTA) && (stages & QAT_BWD_DQ);
-  if ((stages & QAT_BWD_DELTA) && !delta_in_dq) QAT_TRY(qat::launch_bwd_delta(s, o_hp, dout, delta, st));
-  if (stages & QAT_BWD_DQ)
-    QAT_TRY(qat::launch_bwd_dq(s, in, dout, lse, delta, delta_in_dq ? o_hp : nullptr, sm_scale, causal != 0, pfmt,
-                               dq, amax, st));
-  if (stages & QAT_BWD_DKDV)
-    QAT_TRY(qat::launch_bwd_dkdv(s, in, dout, lse, delta, amax, sm_scale, causal != 0, pfmt, dk, dv,
-                                 reinterpret_cast<float*>(ws + L.part), st));
-  return QAT_OK;
+  return qat::bwd_impl(dims, q, k, v, v_scale, o_hp, lse, dout, sm_scale, causal, quant_flags, dq, dk, dv,
+                       workspace, workspace_bytes, stages, true, stream);
 }
 
 int qat_attn_bwd(const qat_attn_dims* dims, const void* q, const void* k, const void* v,
@@ -338,6 +357,7 @@ const char* qat_attn_strerror(int status) {
     case QAT_EUNSUPPORTED: return "unsupported configuration";
     case QAT_EWORKSPACE: return "workspace missing or too small";
     case QAT_EHIP: return "HIP launch failure";
+    case QAT_ESCRATCH: return "problem needs more than the static scratch of qat_attn_bwd_noalloc holds";
     default: return "unknown status";
   }
 }

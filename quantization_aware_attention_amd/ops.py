@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(HERE, "libqat_attn.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "qat_attn.h")
 
 # status codes and flags (values of include/qat_attn.h)
-QAT_OK, QAT_EINVAL, QAT_EUNSUPPORTED, QAT_EWORKSPACE, QAT_EHIP = 0, 1, 2, 3, 4
+QAT_OK, QAT_EINVAL, QAT_EUNSUPPORTED, QAT_EWORKSPACE, QAT_EHIP, QAT_ESCRATCH = 0, 1, 2, 3, 4, 5
+QAT_NOALLOC_SCRATCH_BYTES = 64 << 20
 QAT_DTYPE_BF16, QAT_DTYPE_FP16 = 0, 1
 QAT_P_QUANT = 1 << 0
 QAT_P_E5M2 = 1 << 1
@@ -68,6 +69,8 @@ def lib():
     L.qat_attn_bwd_stages.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, f32, ctypes.c_int, u32, vp, vp, vp, vp, sz,
                                       u32, vp]
     L.qat_attn_bwd_stages.restype = ctypes.c_int
+    L.qat_attn_bwd_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, f32, ctypes.c_int, u32, vp, vp, vp, vp]
+    L.qat_attn_bwd_noalloc.restype = ctypes.c_int
     L.qat_attn_workspace_bytes.argtypes = [dp, u32, ctypes.c_int]
     L.qat_attn_workspace_bytes.restype = sz
     L.qat_quant_v_fp8.argtypes = [dp, vp, vp, vp, vp]
@@ -222,6 +225,31 @@ def attn_bwd(q, k, v, o_hp, lse, dout, sm_scale, causal=False, quant_flags=QAT_P
                                    _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), stages,
                                    _stream())
     _check("qat_attn_bwd_stages", st)
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, o_hp, lse, dout, sm_scale, causal=False, quant_flags=QAT_P_QUANT,
+                     v_scale=None, out=None):
+    """The backward on the library's static scratch (qat_attn_bwd_noalloc):
+    returns (dq, dk, dv); allocates only the outputs when ``out`` is None."""
+    _need_inputs(q, k, v, quant_flags, v_scale)
+    _need(o_hp, "o_hp", q.dtype, q.shape, q.device)
+    _need(lse, "lse", torch.float32, q.shape[:3], q.device)
+    _need(dout, "dout", q.dtype, q.shape, q.device)
+    if out is None:
+        dq, dk = torch.empty_like(q), torch.empty_like(k)
+        dv = torch.empty(k.shape, device=k.device, dtype=q.dtype)
+    else:
+        dq, dk, dv = out
+        _need(dq, "out[0] (dq)", q.dtype, q.shape, q.device)
+        _need(dk, "out[1] (dk)", q.dtype, k.shape, q.device)
+        _need(dv, "out[2] (dv)", q.dtype, k.shape, q.device)
+    _on_device(q=q, k=k, v=v, v_scale=v_scale, o_hp=o_hp, lse=lse, dout=dout, dq=dq, dk=dk, dv=dv)
+    dims = dims_of(q, k)
+    st = lib().qat_attn_bwd_noalloc(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(v_scale), _ptr(o_hp),
+                                    _ptr(lse), _ptr(dout), float(sm_scale), int(bool(causal)), quant_flags,
+                                    _ptr(dq), _ptr(dk), _ptr(dv), _stream())
+    _check("qat_attn_bwd_noalloc", st)
     return dq, dk, dv
 
 

@@ -129,3 +129,15 @@ def test_other_entry_points_validate(L):
     assert L.qat_selftest_fq_scale(0, None, None) == ops.QAT_EINVAL
     assert L.qat_selftest_fq_scale(2, FAKE, None) == ops.QAT_EINVAL
     assert L.qat_selftest_fq_scale(-1, FAKE, None) == ops.QAT_EINVAL
+
+
+def test_noalloc_rejects_oversized_problem_before_any_device_call(L):
+    # long-video size with per-token Q/K/V quantization needs far more than
+    # the static scratch: refused before the library looks at the device
+    d = ops.Dims(1, 40, 32768, 32768, 128, ops.QAT_DTYPE_BF16)
+    flags = ops.QAT_P_QUANT | ops.QAT_QKV_QUANT
+    assert L.qat_attn_workspace_bytes(ctypes.byref(d), flags, 1) > ops.QAT_NOALLOC_SCRATCH_BYTES
+    st = L.qat_attn_bwd_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 0.088, 0, flags,
+                                FAKE, FAKE, FAKE, None)
+    assert st == ops.QAT_ESCRATCH
+    assert L.qat_attn_strerror(ops.QAT_ESCRATCH).startswith(b"problem needs more")
