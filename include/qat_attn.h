@@ -144,9 +144,9 @@ int qat_attn_bwd(const qat_attn_dims* dims, const void* q, const void* k, const 
  *   QAT_BWD_DELTA    Delta = rowsum(dout o o_hp) into the workspace (together
  *                    with QAT_BWD_DQ the dQ kernel forms it, the same bits,
  *                    and no separate pass runs)
- *   QAT_BWD_DQ       dq, and the per-(row, 64-key group) P absmax into the
- *                    workspace (QAT_P_QUANT)
- *   QAT_BWD_DKDV     dk, dv (reads Delta and the P absmax)
+ *   QAT_BWD_DQ       dq, and with QAT_P_QUANT the P-quant absmax record
+ *                    in the workspace (see QAT_P_ABSMAX_MAX_BYTES)
+ *   QAT_BWD_DKDV     dk, dv (reads Delta and that record)
  * A stage reads what earlier stages left in the same workspace: run them in
  * this order, on one stream, with unchanged arguments.  qat_attn_bwd is
  * QAT_BWD_ALL.  Errors as for qat_attn_bwd; QAT_EINVAL for an empty or
@@ -174,11 +174,14 @@ int qat_attn_bwd_stages(const qat_attn_dims* dims, const void* q, const void* k,
  *    address is looked up on the first call on each device); the call
  *    allocates nothing and needs none of its contents to start at zero;
  *  - problems whose scratch exceeds that size (qat_attn_workspace_bytes(dims,
- *    flags, 1) less the dK/dV partial sums) return QAT_ESCRATCH with nothing
- *    enqueued: e.g. the DiT image shape (B1 H24 N4608 D128, 33 MB) fits,
- *    per-token Q/K/V quantization at long-video size does not;
- *  - every dK/dV key block runs whole (no query-range split), so dK and dV
- *    may differ from qat_attn_bwd's in the last bits (fp32 summation order);
+ *    flags, 1) less the dK/dV partial sums and the P-quant absmax record)
+ *    return QAT_ESCRATCH with nothing enqueued: e.g. the DiT image shape
+ *    (B1 H24 N4608 D128, 0.4 MB) fits, per-token Q/K/V quantization at
+ *    long-video size does not;
+ *  - every dK/dV key block runs whole (no query-range split) and the dK/dV
+ *    kernel forms the P-quant absmax itself, so dK and dV may differ from
+ *    qat_attn_bwd's in the last bits (fp32 summation order, and the absmax
+ *    taken from the dK/dV kernel's own scores);
  *  - all calls on one GPU share its scratch: calls that overlap on one GPU
  *    (other streams, other host threads) race and must be serialised by the
  *    caller.
@@ -231,6 +234,15 @@ int qat_attn_sum(const qat_attn_dims* dims, int n_parts, const void* const* part
  * 0 or 1; otherwise the size for these dims and flags (it may be 0).
  */
 size_t qat_attn_workspace_bytes(const qat_attn_dims* dims, uint32_t quant_flags, int pass);
+
+/*
+ * The backward's workspace holds, with QAT_P_QUANT, the dQ kernel's record of
+ * the P-quant absmax per (query row, 64-key group), fp32 B*H*ceil(Nkv/64)*Nq,
+ * for the dK/dV kernel, while that record takes at most this many bytes.
+ * Beyond it the record is left out (the workspace stays linear in Nq and
+ * Nkv) and the dK/dV kernel forms the absmax itself, at some cost in time.
+ */
+#define QAT_P_ABSMAX_MAX_BYTES ((size_t)1 << 30)
 
 /*
  * Per-channel e5m2 quantization of V for the fp8-V path (the e5m2 value path

@@ -20,7 +20,9 @@ inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Workspace layout (each piece 256-byte aligned, in this order):
-//   bwd: delta fp32 [B,H,Nq]; p_amax fp32 [B,H,ceil(Nkv/64),Nq] (P quant only);
+//   bwd: delta fp32 [B,H,Nq]; with P quant, the dQ kernel's record of the
+//   P-quant absmax fp32 [B,H,ceil(Nkv/64),Nq] while it takes at most
+//   QAT_P_ABSMAX_MAX_BYTES (beyond that, the dK/dV kernel forms it itself);
 //   fp32 partial dK/dV of key blocks split over query ranges
 //   fwd and bwd, with K smoothing: the mean's partial sums fp32 [256, D], the
 //   mean fp32 [D] and, without Q/K/V quantization, K - mean (dtype);
@@ -31,24 +33,30 @@ qat::Shape shape_of(const qat_attn_dims& d) { return qat::Shape{d.B, d.H, d.Nq, 
 
 struct Layout {
   size_t delta = 0, amax = 0, part = 0, kpart = 0, kmean = 0, ksm = 0, qh = 0, kh = 0, vh = 0, qs = 0, ks = 0, total = 0;
+  bool side = false;   // the absmax record is part of the workspace
 };
 
-// with_partials = false leaves out the dK/dV tail-split partial sums (the
-// backward then runs every key block whole)
-Layout layout(const qat_attn_dims& d, uint32_t flags, int pass, bool with_partials = true) {
+size_t p_absmax_bytes(const qat_attn_dims& d) {
+  const size_t ng = ((size_t)d.Nkv + QAT_ATTN_P_GROUP - 1) / QAT_ATTN_P_GROUP;
+  return (size_t)d.B * d.H * ng * d.Nq * sizeof(float);
+}
+
+// full = false (the static-scratch backward) leaves out the dK/dV tail-split
+// partial sums (every key block then runs whole) and the absmax record
+Layout layout(const qat_attn_dims& d, uint32_t flags, int pass, bool full = true) {
   Layout L;
   const size_t BH = (size_t)d.B * d.H;
   size_t off = 0;
   if (pass == 1) {
     L.delta = off;
     off += align_up(BH * d.Nq * sizeof(float));
-    if (flags & QAT_P_QUANT) {
+    L.side = full && (flags & QAT_P_QUANT) && p_absmax_bytes(d) <= QAT_P_ABSMAX_MAX_BYTES;
+    if (L.side) {
       L.amax = off;
-      const size_t ng = ((size_t)d.Nkv + QAT_ATTN_P_GROUP - 1) / QAT_ATTN_P_GROUP;
-      off += align_up(BH * ng * d.Nq * sizeof(float));
+      off += align_up(p_absmax_bytes(d));
     }
     L.part = off;
-    if (with_partials) off += align_up(qat::dkdv_part_bytes(shape_of(d)));
+    if (full) off += align_up(qat::dkdv_part_bytes(shape_of(d)));
   }
   if (flags & QAT_SMOOTH_K) {
     L.kpart = off;
@@ -194,7 +202,7 @@ int qat::bwd_impl(const qat_attn_dims* dims, const void* q, const void* k, const
     in = prepared_inputs(L, quant_flags, q, k, v, v_scale, ws);
   }
   float* delta = reinterpret_cast<float*>(ws + L.delta);
-  float* amax = (quant_flags & QAT_P_QUANT) ? reinterpret_cast<float*>(ws + L.amax) : nullptr;
+  float* amax = L.side ? reinterpret_cast<float*>(ws + L.amax) : nullptr;
   const int pfmt = pfmt_of(quant_flags);
   // Delta together with dQ: the dQ kernel forms it for its rows (bit for bit
   // as the separate pass) and publishes it for dK/dV, one launch fewer

@@ -12,18 +12,18 @@
 //  * dQ kernel: a workgroup of 4 waves owns 128 query rows; like the forward,
 //    each wave computes S^T = K Q^T and dP^T = V dO^T so every lane owns one
 //    query row (Q^T, dO^T stay in registers, K/V tiles stream through LDS);
-//    dQ^T = K^T dS^T reads K^T through ds_read_b64_tr_b16.  Because a lane
-//    holds a query row's 64-key group, this kernel also records the P-quant
-//    absmax of every (row, group) for the dK/dV kernel.
+//    dQ^T = K^T dS^T reads K^T through ds_read_b64_tr_b16.  dQ does not use
+//    P^, so this kernel forms no P-quant scale.
 //  * dK/dV kernel: a workgroup of 8 waves owns 128 keys (two P groups);
 //    each wave keeps its 32 keys' K^T (and V^T) in registers and computes
 //    S = Q K^T (and dP = dO V^T) with one lane per key, so P^ and dS are
 //    already the operands of dV^T = dO^T P^ and dK^T = Q^T dS (Q and dO
 //    tiles go through LDS, read row-major for S/dP and transposed for dV/dK).
 //    Half the waves accumulate dV, half dK, so each holds one accumulator.
-//    A key-per-lane layout has a query's 64 keys spread over 64 lanes of two
-//    waves; reading the absmax recorded by the dQ kernel replaces that
-//    cross-lane reduction.
+//    A query's 64-key P group spans the 32 keys of two waves: each reduces
+//    its half over lanes, the two exchange the halves through LDS across the
+//    workgroup barrier, and the P^ and dV of a block follow one iteration
+//    later.  Nothing of size Nq x Nkv leaves the kernels.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -92,8 +92,8 @@ struct BwdArgs {
   const void* dout;
   const float* lse;
   const float* delta;
-  float* p_amax;        // [BH][NG][Nq]
-  const float* p_amax_in;
+  float* p_amax;        // dQ: P-quant absmax per (row, 64-key group) [BH][NG][Nq], or null
+  const float* p_amax_in;   // dK/dV: the same, or null (formed in the dK/dV kernel)
   void* dq;
   void* dk;
   void* dv;
@@ -369,11 +369,11 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
           if (lane_g4 >= Nkv - kv0 - c || (CAUSAL && lane_dq > q0 - kv0 - c)) p[kb][r] = 0.0f;
         }
     }
+    if (PQ >= 0 && a.p_amax) {   // the P-quant absmax of the row's group, for the dK/dV kernel
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pmax = fmaxf(pmax, p[kb][r]);
-    if constexpr (PQ >= 0) {
+        for (int r = 0; r < 16; ++r) pmax = fmaxf(pmax, p[kb][r]);
       pmax = max_xor32(pmax);
       if (g == 0 && qi < Nq) a.p_amax[((size_t)bh * a.NG + t) * Nq + qi] = pmax;
     }
@@ -416,9 +416,6 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
     if (t + 1 < ntiles) finish_tile(buf ^ 1);
     __syncthreads();
   }
-  // causal rows whose every later tile was skipped still record zero-free
-  // groups only for tiles they visited; the dK/dV kernel never reads the
-  // others (the keys are masked there).
   // K smoothing: dQ is taken for the original K = (K - k_mean) + k_mean
   float rs = 0.0f;
   if constexpr (smooth) rs = sum_xor32(ds_rowsum);
@@ -456,17 +453,21 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 // of the K^T / V^T operands, which fits the 256 registers of two waves per
 // SIMD: while one wave waits on an MFMA or an LDS read the other issues, and
 // the two waves' vector work runs under each other's matrix work.
+// The absmax of a (query, 64-key group) needs the keys of two P waves (kw,
+// kw ^ 1): each publishes its 32-key maximum per query of block i, and after
+// the barrier both form the group's scales and quantize P(i), read back
+// from LDS.
 // Iteration i (one workgroup barrier at its end):
-//   P wave:  S(i+1) MFMAs; vector work of block i (P(i) to LDS, P^(i));
-//            dV MFMAs of block i;
+//   P wave:  S(i+1) MFMAs; P(i) to LDS and its 32-key maxima; scales and
+//            P^ of block i-1; dV MFMAs of block i-1;
 //   dS wave: dP(i) MFMAs; vector work of block i-1 (P(i-1) from LDS, written
 //            in iteration i-1); dK MFMAs of block i-1;
 //   all:     block i+2 (loaded in iteration i-1) written to LDS slot
 //            (i+2) % 4, block i+3 loaded into registers.
 // LDS slot reads in iteration i touch blocks i-1 .. i+1 only, so the slot
 // written in iteration i was last read in iteration i-1, before the barrier;
-// the P buffer of parity i&1 is rewritten in iteration i+2, after the
-// barrier that ends the dS wave's read of it in iteration i+1.
+// the P buffer and the maxima of parity i&1 are rewritten in iteration i+2,
+// after the barrier that ends their reads in iteration i+1.
 // Maximum over aligned groups of N consecutive lanes (N = 8 or 16) by DPP:
 // the partner exchanges lane ^ 1, lane ^ 2, the mirror within eight lanes and
 // (N = 16) the mirror within sixteen leave every lane with its group's max.
@@ -485,12 +486,52 @@ __device__ __forceinline__ float row_max_dpp(float x) {
   return x;
 }
 
+// Maximum over the 32 lanes of each lane half, for each of the 16 registers
+// of x (probabilities: >= 0 and never NaN, so the unsigned order of their
+// bit patterns is their order), by a transposing reduction that halves the
+// register count at every step: v_permlane16_swap pairs the two 16-lane rows
+// of a half (lane ^ 16), then DPP pairs lane ^ 8 (row rotation by 8),
+// l <-> 7 - l within eight lanes (half-row mirror), lane ^ 2 and lane ^ 1
+// (quad permutations).  At each step a lane keeps the register of the pair
+// that its lane bit selects, combined with the same register of its
+// partner, whose bit is the other one.  Lane l ends with the maximum of
+// register (l >> 1) & 15 of its half.
+__device__ __forceinline__ float half_max16(const f32x16& x, int lane) {
+  uint32_t t[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {   // bit 4: lanes < 16 of a half keep x[k], the others x[k + 8]
+    // (elements copied out first: a bit cast of a vector element expression
+    // reads the vector's first element in this compiler)
+    const float lo = x[k], hi = x[k + 8];
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, lo),
+                                                    __builtin_bit_cast(uint32_t, hi), false, false);
+    t[k] = max((uint32_t)r[0], (uint32_t)r[1]);
+  }
+  auto pair = [](uint32_t lo, uint32_t hi, bool bit, auto CTRL) {
+    constexpr int c = decltype(CTRL)::value;
+    const uint32_t ml = max(lo, (uint32_t)__builtin_amdgcn_mov_dpp((int)lo, c, 0xF, 0xF, true));
+    const uint32_t mh = max(hi, (uint32_t)__builtin_amdgcn_mov_dpp((int)hi, c, 0xF, 0xF, true));
+    return bit ? mh : ml;
+  };
+  const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+  uint32_t u[4], v[2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) u[k] = pair(t[k], t[k + 4], b3, std::integral_constant<int, 0x128>{});   // row_ror:8
+#pragma unroll
+  for (int k = 0; k < 2; ++k) v[k] = pair(u[k], u[k + 2], b2, std::integral_constant<int, 0x141>{});   // row_half_mirror
+  const uint32_t m = pair(v[0], v[1], b1, std::integral_constant<int, 0x4E>{});                        // quad_perm [2,3,0,1]
+  return __builtin_bit_cast(float, max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, true)));
+}
+
 constexpr int DPR_BN = 128;    // keys per workgroup
 constexpr int DPR_BQ = 32;     // queries per block
 constexpr int DPR_SLOTS = 4;   // LDS slots of Q/dO blocks
 
-template <class DT, int D, bool CAUSAL, int PQ, int IN>
+// AMX (P quant only): the P waves form the group absmax themselves (above);
+// otherwise they read the absmax the dQ kernel recorded per (query, group).
+template <class DT, int D, bool CAUSAL, int PQ, int IN, bool AMX>
 __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
+  static_assert(!AMX || PQ >= 0, "in-kernel absmax is for P quant");
   constexpr bool VFP8 = IN == IN_VFP8;
   constexpr bool QKS = IN == IN_QKS;
   constexpr int TILE = DPR_BQ * D * 2;
@@ -498,6 +539,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
   constexpr int NKS = D / 16;
   constexpr int FQF = PQ >= 0 ? PQ : 0;
   constexpr int NGW = DPR_BN / 64;          // 64-key P groups of the workgroup
+  constexpr bool SIDE = PQ >= 0 && !AMX;    // P-quant absmax read from the dQ kernel's record
   constexpr int CPR = D / 8;                // 16-byte chunks per row
   constexpr int CHUNKS = DPR_BQ * CPR;      // chunks per tensor and block
   constexpr int NCH = 2 * CHUNKS / 512;     // staged chunks per thread (Q and dO together)
@@ -512,8 +554,18 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float d_s[DPR_SLOTS][DPR_BQ];
   __shared__ __attribute__((aligned(16))) float sq_s[QKS ? DPR_SLOTS : 1][DPR_BQ];
   __shared__ __attribute__((aligned(16))) float cq_s[QKS ? DPR_SLOTS : 1][DPR_BQ];   // c * s_q (exponent scale)
-  __shared__ __attribute__((aligned(16))) float qs_s[DPR_SLOTS][NGW][DPR_BQ];
-  __shared__ __attribute__((aligned(16))) float qr_s[DPR_SLOTS][NGW][DPR_BQ];
+  // rows of +inf read as M by key lanes past Nkv, so that their p is 0 (and
+  // stays out of the P-quant absmax)
+  __shared__ __attribute__((aligned(16))) float minf_s[DPR_SLOTS][DPR_BQ];
+  // SIDE: the P-quant scale pairs of the workgroup's two 64-key groups per
+  // staged block.  AMX: each P wave's maximum over its 32 keys per query
+  // ([block parity][wave][query]), and the scale pair of the wave's 64-key
+  // group that the wave forms from its own and its partner's maxima.
+  __shared__ __attribute__((aligned(16))) float qs_s[SIDE ? DPR_SLOTS : 1][NGW][DPR_BQ];
+  __shared__ __attribute__((aligned(16))) float qr_s[SIDE ? DPR_SLOTS : 1][NGW][DPR_BQ];
+  __shared__ __attribute__((aligned(16))) float pm_s[AMX ? 2 : 1][4][DPR_BQ];
+  __shared__ __attribute__((aligned(16))) float qsw_s[AMX ? 4 : 1][DPR_BQ];
+  __shared__ __attribute__((aligned(16))) float qrw_s[AMX ? 4 : 1][DPR_BQ];
   __shared__ __attribute__((aligned(16))) f32x4 p_s[2][4][4][64];   // [block parity][key quarter][reg quarter][lane]
   // fp8 V: dO * v_scale rows scaled by a power of two and rounded to fp16 (the
   // dS wave's dP operand; dV keeps the plain dO tile), and each row's inverse
@@ -547,7 +599,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
   const int kj = k0w + l32;
   const int Nq = a.Nq, Nkv = a.Nkv;
   const int lgrp = kw >> 1;               // this wave's 64-key group within the workgroup
-  const int grp0 = k0 / 64;
   const uint16_t* qp = (const uint16_t*)a.q + (size_t)bh * Nq * D;
   const uint16_t* dop = (const uint16_t*)a.dout + (size_t)bh * Nq * D;
 
@@ -567,9 +618,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
   // head's Nq rows, so rows past Nq read as zeros and each address is a fixed
   // per-thread offset plus the block's uniform row offset.  Per-query
   // vectors, one wave each so that control flow stays uniform: wave 0 LSE
-  // (lanes 0-31) and Delta (lanes 32-63), wave 1 the P-quant absmax of the
-  // workgroup's two 64-key groups (group lane / 32), wave 2 the per-token
-  // query scale (per-token codes only).
+  // (lanes 0-31) and Delta (lanes 32-63), wave 1 (SIDE) the P-quant absmax
+  // of the workgroup's two 64-key groups (group lane / 32), wave 2 the
+  // per-token query scale (per-token codes only).
   u32x4 stg[NCH];
   float stv = 0.0f;
   const __amdgpu_buffer_rsrc_t rsrc_q = __builtin_amdgcn_make_buffer_rsrc((void*)qp, 0, Nq * D * 2, 0x00020000);
@@ -582,13 +633,13 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
     if (tid < D) vs_s[tid] = a.v_scale[(size_t)bh * D + tid];
     __syncthreads();
   }
-  const float* v_src = nullptr;   // wave 0-2: this lane's vector source (per head), else unused
+  const float* v_src = nullptr;   // waves 0-2: this lane's vector source (per head), else unused
   bool v_live = false;            // the lane's vector entry exists (wave 1: group inside the keys)
   if (w == 0) {
     v_src = (lane < 32 ? a.lse : a.delta) + (size_t)bh * Nq;
     v_live = true;
-  } else if (w == 1 && PQ >= 0) {
-    const int gq = grp0 + g;
+  } else if (w == 1 && SIDE) {
+    const int gq = k0 / 64 + g;
     v_live = g < NGW && gq < a.NG;
     v_src = a.p_amax_in + ((size_t)bh * a.NG + (v_live ? gq : 0)) * Nq;
   } else if (w == 2 && QKS && lane < 32) {
@@ -603,7 +654,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
       stg[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                             st_tensor(j) ? rsrc_do : rsrc_q, row * D * 2 + ch * 16, q0 * D * 2, 0));
     }
-    if (w < 3 && v_live) stv = v_src[min(q0 + l32, Nq - 1)];
+    if (v_live) stv = v_src[min(q0 + l32, Nq - 1)];
   };
   // (slot: compile-time b % DPR_SLOTS, so the LDS addresses fold into offsets)
   auto write_tiles = [&](auto SLOTc) __attribute__((always_inline)) {
@@ -642,11 +693,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
       // M = +inf for rows past Nq: their p = exp2(S c - M) is exactly 0
       float* dst = lane < 32 ? &m_s[slot][l32] : &d_s[slot][l32];
       *dst = lane < 32 ? (ok ? v * LOG2E : INFINITY) : (ok ? v : 0.0f);
-    } else if (w == 1 && PQ >= 0) {
+    } else if (w == 1 && SIDE) {
       const FqScale fs = fq_scale<FQF>(ok ? v : 0.0f);
       if (g < NGW) {
-        qs_s[slot][g][l32] = fs.s;
-        qr_s[slot][g][l32] = fs.r;
+        qs_s[SIDE ? slot : 0][g][l32] = fs.s;
+        qr_s[SIDE ? slot : 0][g][l32] = fs.r;
       }
     } else if (w == 2 && QKS && lane < 32) {
       sq_s[slot][l32] = ok ? v : 1.0f;
@@ -673,12 +724,16 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
     }
     f32x4* pz = &p_s[0][0][0][0];
     for (int k = tid; k < 2 * 4 * 4 * 64; k += 512) pz[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    if (AMX && tid < 2 * 4 * DPR_BQ) (&pm_s[0][0][0])[tid] = 0.0f;
+    if (tid < DPR_SLOTS * DPR_BQ) (&minf_s[0][0])[tid] = INFINITY;
     if (tid < DPR_BQ) {
       for (int sl = z0; sl < DPR_SLOTS; ++sl) {
         m_s[sl][tid] = 0.0f;
         d_s[sl][tid] = 0.0f;
+        if constexpr (SIDE) {
 #pragma unroll
-        for (int gq = 0; gq < NGW; ++gq) qs_s[sl][gq][tid] = qr_s[sl][gq][tid] = 0.0f;
+          for (int gq = 0; gq < NGW; ++gq) qs_s[SIDE ? sl : 0][gq][tid] = qr_s[SIDE ? sl : 0][gq][tid] = 0.0f;
+        }
         if constexpr (QKS) sq_s[sl][tid] = cq_s[sl][tid] = 0.0f;
         if constexpr (VFP8) es_s[VFP8 ? sl : 0][tid] = 0.0f;
       }
@@ -729,22 +784,25 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
     for (int db = 0; db < NDB; ++db) acc[db] = (f32x16){};
     // score buffers: P wave S(i) / S(i+1), dS wave dP(i-1) / dP(i), by parity
     f32x16 sb[2] = {(f32x16){}, (f32x16){}};
-    uint32_t op[8];   // packed P^ (P wave) or dS (dS wave) of the block: query half h = words 4h .. 4h+3
+    uint32_t op[8];   // packed P^ (P wave) or dS (dS wave) of block i-1: query half h = words 4h .. 4h+3
 #pragma unroll
     for (int j = 0; j < 8; ++j) op[j] = 0u;
     // per-query vectors of a register quarter, double-buffered by quarter
-    // parity: P wave M, c s_q (per-token codes), P-quant s and r; dS wave
-    // Delta, s_q (per-token codes) and the quarter's P from LDS
-    f32x4 v0[2], v1[2], v2[2], v3[2];
+    // parity: P wave M and c s_q (per-token codes) of block i, P-quant s, r
+    // and the quarter's P of block i-1 (from LDS); dS wave Delta, s_q
+    // (per-token codes) and the quarter's P of block i-1
+    f32x4 v0[2], v1[2], v2[2], v3[2], pq[2];
+    // P wave: M rows of this lane's key (+inf rows past Nkv)
+    const float* m_lane = kj < Nkv ? &m_s[0][0] : &minf_s[0][0];
 
     // MFMA step st of iteration i: st < NKS the score k-step st (Q or dO row
     // fragment against the K^T or V^T registers), else the accumulator step
     // (h, db) (transposed dO or Q fragment against the packed operand).
     auto tiles = [&](auto SLOTc, const char*& X, const char*& Y) __attribute__((always_inline)) {
       constexpr int SL = decltype(SLOTc)::value;   // slot of block i
-      if constexpr (R == 0) {
+      if constexpr (R == 0) {   // dV of block i - 1 (AMX) or i
         X = q_s[(SL + 1) & (DPR_SLOTS - 1)];
-        Y = do_s[SL];
+        Y = do_s[AMX ? (SL + DPR_SLOTS - 1) & (DPR_SLOTS - 1) : SL];
       } else {
         X = VFP8 ? dos_s[VFP8 ? SL : 0] : do_s[SL];
         Y = q_s[(SL + DPR_SLOTS - 1) & (DPR_SLOTS - 1)];
@@ -768,20 +826,30 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
     };
     // ---- vector work of a register quarter u (registers 4u .. 4u+3: queries
     // 8u + 4g + 0..3 of the block), its vectors in buffer u & 1
-    auto read_quarter = [&](int u, int slot, int par) __attribute__((always_inline)) {
+    auto read_quarter = [&](int u, int slot, int par) __attribute__((always_inline)) {   // dS wave, block i-1
       const int ql = 8 * u + 4 * g, bsel = u & 1;
-      if constexpr (R == 0) {
-        v0[bsel] = *reinterpret_cast<const f32x4*>(&m_s[slot][ql]);
-        if constexpr (QKS) v1[bsel] = *reinterpret_cast<const f32x4*>(&cq_s[slot][ql]);
-        if constexpr (PQ >= 0) {
-          v2[bsel] = *reinterpret_cast<const f32x4*>(&qs_s[slot][lgrp][ql]);
-          v3[bsel] = *reinterpret_cast<const f32x4*>(&qr_s[slot][lgrp][ql]);
-        }
-      } else {
-        v0[bsel] = *reinterpret_cast<const f32x4*>(&d_s[slot][ql]);
-        if constexpr (QKS) v1[bsel] = *reinterpret_cast<const f32x4*>(&sq_s[slot][ql]);
-        if constexpr (VFP8) v1[bsel] = *reinterpret_cast<const f32x4*>(&es_s[VFP8 ? slot : 0][ql]);
-        v2[bsel] = p_s[par][kw][u][lane];   // P of block i-1, written by the P wave
+      v0[bsel] = *reinterpret_cast<const f32x4*>(&d_s[slot][ql]);
+      if constexpr (QKS) v1[bsel] = *reinterpret_cast<const f32x4*>(&sq_s[slot][ql]);
+      if constexpr (VFP8) v1[bsel] = *reinterpret_cast<const f32x4*>(&es_s[VFP8 ? slot : 0][ql]);
+      v2[bsel] = p_s[par][kw][u][lane];   // P of block i-1, written by the P wave
+    };
+    auto read_m = [&](int u, int slot) __attribute__((always_inline)) {   // P wave, block i
+      const int ql = 8 * u + 4 * g, bsel = u & 1;
+      v0[bsel] = *reinterpret_cast<const f32x4*>(m_lane + slot * DPR_BQ + ql);
+      if constexpr (QKS) v1[bsel] = *reinterpret_cast<const f32x4*>(&cq_s[slot][ql]);
+      if constexpr (SIDE) {   // and the staged scale pairs of block i
+        v2[bsel] = *reinterpret_cast<const f32x4*>(&qs_s[SIDE ? slot : 0][lgrp][ql]);
+        v3[bsel] = *reinterpret_cast<const f32x4*>(&qr_s[SIDE ? slot : 0][lgrp][ql]);
+      }
+    };
+    auto read_pq = [&](int u, int par) __attribute__((always_inline)) {   // P wave, P of block i-1
+      pq[u & 1] = p_s[par][kw][u][lane];
+    };
+    auto read_sc = [&](int u) __attribute__((always_inline)) {   // P wave, scales of block i-1
+      const int ql = 8 * u + 4 * g, bsel = u & 1;
+      if constexpr (AMX) {
+        v2[bsel] = *reinterpret_cast<const f32x4*>(&qsw_s[kw][ql]);
+        v3[bsel] = *reinterpret_cast<const f32x4*>(&qrw_s[kw][ql]);
       }
     };
     // P wave: p = exp2(S c - M) in place (S of block i)
@@ -795,24 +863,61 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
         S[r] = fast_exp2(__builtin_fmaf(sr, cr, -v0[bsel][e]));
       }
     };
-    // P wave: hand P to the dS wave, P^ = FQ(P) per (query, 64-key group) packed
-    auto finish_p = [&](int u, const f32x16& S, int par) __attribute__((always_inline)) {
-      const int bsel = u & 1;
+    // P wave: P of block i to LDS (the dS wave's operand in iteration i+1,
+    // and this wave's P^ of block i in iteration i+1)
+    auto store_p = [&](int u, const f32x16& S, int par) __attribute__((always_inline)) {
       p_s[par][kw][u][lane] = (f32x4){S[4 * u], S[4 * u + 1], S[4 * u + 2], S[4 * u + 3]};
+    };
+    // P wave: the 64-key group absmax of block i-1 per query from the two
+    // P waves' 32-key maxima, and its scale pair for this wave's quarters
+    uint32_t pm_own = 0u, pm_par = 0u;
+    auto read_pm = [&](int par) __attribute__((always_inline)) {
+      if constexpr (AMX) {
+        pm_own = __builtin_bit_cast(uint32_t, pm_s[par][kw][l32]);
+        pm_par = __builtin_bit_cast(uint32_t, pm_s[par][kw ^ 1][l32]);
+      }
+    };
+    auto group_scales = [&]() __attribute__((always_inline)) {
+      if constexpr (AMX) {
+        const FqScale fs = fq_scale<FQF>(__builtin_bit_cast(float, max(pm_own, pm_par)));   // p >= 0
+        if (g == 0) {
+          qsw_s[kw][l32] = fs.s;
+          qrw_s[kw][l32] = fs.r;
+        }
+        // lane-to-lane through this wave's own LDS words: in order within
+        // the wave, kept in order by the compiler
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+    };
+    // P wave: P^ = FQ(P) per (query, 64-key group) of quarter u, packed, from
+    // P of block i-1 read back (AMX) or of block i in registers
+    auto quantize = [&](int u, const f32x4& x4) __attribute__((always_inline)) {
+      const int bsel = u & 1;
       uint32_t w0, w1;
       if constexpr (PQ >= 0) {
         const FqScale f4[4] = {{v2[bsel][0], v3[bsel][0]}, {v2[bsel][1], v3[bsel][1]},
                                {v2[bsel][2], v3[bsel][2]}, {v2[bsel][3], v3[bsel][3]}};
-        const float x[4] = {S[4 * u], S[4 * u + 1], S[4 * u + 2], S[4 * u + 3]};
+        const float x[4] = {x4[0], x4[1], x4[2], x4[3]};
         const f32x4 xq = fq_quad<FQF>(x, f4);
         w0 = DT::pack2(xq[0], xq[1]);
         w1 = DT::pack2(xq[2], xq[3]);
       } else {
-        w0 = DT::pack2(S[4 * u], S[4 * u + 1]);
-        w1 = DT::pack2(S[4 * u + 2], S[4 * u + 3]);
+        w0 = DT::pack2(x4[0], x4[1]);
+        w1 = DT::pack2(x4[2], x4[3]);
       }
       op[2 * u] = w0;
       op[2 * u + 1] = w1;
+    };
+    // P wave: this wave's 32-key maximum per query of block i, for both P
+    // waves of the group (p >= 0, masked entries are 0)
+    auto publish_max = [&](const f32x16& S, int par) __attribute__((always_inline)) {
+      if constexpr (AMX) {
+        const float m = half_max16(S, lane);
+        const int r = (lane >> 1) & 15;
+        pm_s[par][kw][4 * g + 8 * (r >> 2) + (r & 3)] = m;
+      }
     };
     // dS wave: dS = P o (dP - Delta) for block i-1
     auto finish_ds = [&](int u, const f32x16& DP) __attribute__((always_inline)) {
@@ -834,15 +939,34 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
     auto slice = [&](int j, auto SLOTc, f32x16& CUR, int par) __attribute__((always_inline)) {
       constexpr int SL = decltype(SLOTc)::value;
       if constexpr (R == 0) {
-        constexpr int slot = SL;                                       // block i
-        switch (j) {
-          case 0: read_quarter(0, slot, par); read_quarter(1, slot, par); form_p(0, CUR); break;
-          case 1: finish_p(0, CUR, par); form_p(1, CUR); read_quarter(2, slot, par); break;
-          case 2: finish_p(1, CUR, par); read_quarter(3, slot, par); break;
-          case 3: form_p(2, CUR); break;
-          case 4: finish_p(2, CUR, par); form_p(3, CUR); break;
-          case 5: finish_p(3, CUR, par); break;
-          default: break;
+        // block i: P to LDS and this wave's maximum (par = i & 1); block i-1:
+        // scales, P^ for the dV MFMAs of this iteration (par ^ 1)
+        constexpr int slot = SL;
+        auto cur4 = [&](int u) {
+          return (f32x4){CUR[4 * u], CUR[4 * u + 1], CUR[4 * u + 2], CUR[4 * u + 3]};
+        };
+        if constexpr (AMX) {
+          switch (j) {
+            case 0: read_pm(par ^ 1); read_m(0, slot); read_m(1, slot); form_p(0, CUR); break;
+            case 1: group_scales(); read_pq(0, par ^ 1); read_pq(1, par ^ 1); form_p(1, CUR);
+                    store_p(0, CUR, par); store_p(1, CUR, par); read_m(2, slot); read_m(3, slot); break;
+            case 2: read_sc(0); read_sc(1); form_p(2, CUR); break;
+            case 3: quantize(0, pq[0]); quantize(1, pq[1]); read_sc(2); read_sc(3); read_pq(2, par ^ 1);
+                    read_pq(3, par ^ 1); form_p(3, CUR); store_p(2, CUR, par); store_p(3, CUR, par); break;
+            case 4: quantize(2, pq[0]); quantize(3, pq[1]); break;
+            case 5: publish_max(CUR, par); break;
+            default: break;
+          }
+        } else {   // block i throughout: P to LDS and P^ in the same iteration
+          switch (j) {
+            case 0: read_m(0, slot); read_m(1, slot); form_p(0, CUR); break;
+            case 1: store_p(0, CUR, par); quantize(0, cur4(0)); form_p(1, CUR); read_m(2, slot); break;
+            case 2: store_p(1, CUR, par); quantize(1, cur4(1)); read_m(3, slot); break;
+            case 3: form_p(2, CUR); break;
+            case 4: store_p(2, CUR, par); quantize(2, cur4(2)); form_p(3, CUR); break;
+            case 5: store_p(3, CUR, par); quantize(3, cur4(3)); break;
+            default: break;
+          }
         }
       } else {
         constexpr int slot = (SL + DPR_SLOTS - 1) & (DPR_SLOTS - 1);   // block i - 1
@@ -888,9 +1012,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
       f32x16& SO = R == 0 ? sb[PAR ^ 1] : sb[PAR];
       f32x16& CUR = R == 0 ? sb[PAR] : sb[PAR ^ 1];
       constexpr int pb = R == 0 ? PAR : PAR ^ 1;   // P buffer written (P wave) / read (dS wave)
-      // the block of the vector work exists for this wave (else its operand
-      // words are zeroed, and the accumulator MFMAs add nothing)
-      const bool ok = R == 0 ? (i < NB && active(i)) : (i >= 1 && active(i - 1));
+      // the block of the accumulator MFMAs (i for the P wave without AMX,
+      // else i - 1) exists for this wave (else its operand words are zeroed,
+      // and the accumulator MFMAs add nothing)
+      const bool ok = (R == 0 && !AMX) ? (i < NB && active(i)) : (i >= 1 && active(i - 1));
       const bool stw = i + 2 < NB, stl = i + 3 < NB;
       const char *X, *Y;
       tiles(SLOTc, X, Y);
@@ -915,11 +1040,13 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
           step(cur, st, SO);
         }
         slice(j, SLOTc, CUR, pb);
-        // operand words of an absent block: zero before the accumulator
-        // MFMAs of query half 0 (group 4) and half 1 (group 6) read them
-        if ((j == 2 || j == 5) && !ok) {
+        // operand words of an absent block: zero after they are formed and
+        // before the accumulator MFMAs of query half 0 (group 4) and half 1
+        // (group 6) read them
+        constexpr int zlo = (R == 0 && AMX) ? 3 : 2;
+        if ((j == zlo || j == 5) && !ok) {
 #pragma unroll
-          for (int w4 = 0; w4 < 4; ++w4) op[(j == 2 ? 0 : 4) + w4] = 0u;
+          for (int w4 = 0; w4 < 4; ++w4) op[(j == zlo ? 0 : 4) + w4] = 0u;
         }
         if (j == 0 && stw) write_tiles(std::integral_constant<int, (SL + 2) & (DPR_SLOTS - 1)>{});
         if (j == 1 && stw) write_vec(i + 2, std::integral_constant<int, (SL + 2) & (DPR_SLOTS - 1)>{});
@@ -1012,7 +1139,13 @@ struct DqK {
 template <class DT, int D, bool CAUSAL, int PQ, int IN>
 struct DkvK {
   static void run(dim3 g, const BwdArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((dkdv_pair_kernel<DT, D, CAUSAL, PQ, IN>), g, dim3(512), 0, st, a);
+    if constexpr (PQ >= 0) {
+      if (!a.p_amax_in) {
+        hipLaunchKernelGGL((dkdv_pair_kernel<DT, D, CAUSAL, PQ, IN, true>), g, dim3(512), 0, st, a);
+        return;
+      }
+    }
+    hipLaunchKernelGGL((dkdv_pair_kernel<DT, D, CAUSAL, PQ, IN, false>), g, dim3(512), 0, st, a);
   }
 };
 

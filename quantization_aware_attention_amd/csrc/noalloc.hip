@@ -1,6 +1,6 @@
 // qat_attn_bwd_noalloc: the backward with no allocation and no workspace
-// argument.  Its scratch (Delta, the P-quant absmax per row and key group,
-// and with Q/K/V quantization the quantized copies) lives in one file-scope
+// argument.  Its scratch (Delta, and with Q/K/V quantization the quantized
+// copies) lives in one file-scope
 // device array, `scratch`, that every GPU the library runs on holds from
 // module load until the process ends.  In host code `scratch` names a
 // host-side stand-in, not the device array: its device address is taken once

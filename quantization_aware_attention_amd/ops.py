@@ -19,6 +19,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "qat_attn.h")
 # status codes and flags (values of include/qat_attn.h)
 QAT_OK, QAT_EINVAL, QAT_EUNSUPPORTED, QAT_EWORKSPACE, QAT_EHIP, QAT_ESCRATCH = 0, 1, 2, 3, 4, 5
 QAT_NOALLOC_SCRATCH_BYTES = 64 << 20
+QAT_P_ABSMAX_MAX_BYTES = 1 << 30
 QAT_DTYPE_BF16, QAT_DTYPE_FP16 = 0, 1
 QAT_P_QUANT = 1 << 0
 QAT_P_E5M2 = 1 << 1

@@ -49,9 +49,11 @@ def rel_l2(x, y) -> float:
     return float(np.linalg.norm(x - y) / den) if den > 0 else float(np.linalg.norm(x - y))
 
 
-def run_gpu(w: W.Workload, inp: dict, p_quant=True, backward=True):
+def run_gpu(w: W.Workload, inp: dict, p_quant=True, backward=True, bwd_entry="workspace"):
     """Forward (+ backward) on the GPU; returns dict of numpy float64 arrays
-    plus the fp8 V codes / scales when V is fp8."""
+    plus the fp8 V codes / scales when V is fp8.  bwd_entry "noalloc" runs
+    the backward through qat_attn_bwd_noalloc (static scratch, P-quant
+    absmax formed inside the dK/dV kernel)."""
     from quantization_aware_attention_amd import ops
     q = to_dev(inp["q_bits"], w.dtype)
     k = to_dev(inp["k_bits"], w.dtype)
@@ -67,7 +69,8 @@ def run_gpu(w: W.Workload, inp: dict, p_quant=True, backward=True):
     o, o_hp, lse = ops.attn_fwd(q, k, v, w.sm_scale, w.causal, flags, v_scale=v_scale)
     res = {"o": o, "o_hp": o_hp, "lse": lse}
     if backward:
-        dq, dk, dv = ops.attn_bwd(q, k, v, o_hp, lse, do, w.sm_scale, w.causal, flags, v_scale=v_scale)
+        bwd = ops.attn_bwd_noalloc if bwd_entry == "noalloc" else ops.attn_bwd
+        dq, dk, dv = bwd(q, k, v, o_hp, lse, do, w.sm_scale, w.causal, flags, v_scale=v_scale)
         res.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     out.update({n: to_np(t) for n, t in res.items()})

@@ -31,6 +31,21 @@ def test_exports_every_declared_symbol(L):
         assert hasattr(L, n), n
 
 
+def test_binding_constants_match_the_header():
+    import re
+    vals = {}
+    for line in open(ops.HEADER):
+        m = re.match(r"#define (QAT_\w+)\s+(.+?)\s*(/\*.*)?$", line)
+        if m and m.group(1) != "QAT_ATTN_H":
+            expr = re.sub(r"\(size_t\)|(?<=\d)u\b", "", m.group(2))
+            vals[m.group(1)] = eval(expr, {}, dict(vals))
+    for name, v in vals.items():
+        if hasattr(ops, name):
+            assert getattr(ops, name) == v, name
+    for name in ("QAT_P_QUANT", "QAT_ESCRATCH", "QAT_NOALLOC_SCRATCH_BYTES", "QAT_P_ABSMAX_MAX_BYTES"):
+        assert name in vals and hasattr(ops, name), name
+
+
 def test_constants(L):
     assert L.qat_attn_p_group() == 64
     assert L.qat_attn_strerror(ops.QAT_EINVAL) == b"invalid argument"
@@ -95,9 +110,9 @@ def test_workspace_layout():
     assert ops.workspace_bytes(d, ops.QAT_P_QUANT, 0) == 0
     up = lambda x: -(-x // 256) * 256
     delta = up(2 * 3 * 100 * 4)
-    amax = up(2 * 3 * 3 * 100 * 4)            # ceil(130 / 64) = 3 groups
     # fp32 dK/dV partials: up to 4 query ranges per 128-key block, at most 768 in all
     part = up(min(6 * 2 * 4, 768) * 2 * 128 * 128 * 4)
+    amax = up(2 * 3 * 3 * 100 * 4)            # P-quant absmax record: ceil(130 / 64) = 3 groups
     assert ops.workspace_bytes(d, 0, 1) == delta + part
     assert ops.workspace_bytes(d, ops.QAT_P_QUANT, 1) == delta + amax + part
     qkv = up(6 * 100 * 128 * 2) + 2 * up(6 * 130 * 128 * 2) + up(6 * 100 * 4) + up(6 * 130 * 4)
@@ -112,6 +127,14 @@ def test_workspace_layout():
     assert ops.workspace_bytes(d, ops.QAT_QKV_QUANT | ops.QAT_SMOOTH_K, 0) == sk + qkv
     big = D(1, 24, 4608, 4608, 128, 0)        # 864 key blocks: capped at 768 partial blocks
     assert ops.workspace_bytes(big, 0, 1) == up(24 * 4608 * 4) + up(768 * 2 * 128 * 128 * 4)
+    # the absmax record is bounded: at 40 heads of 32768 it would take 2.7 GB,
+    # so it is left out and the workspace stays linear in the sequence length
+    lv = D(1, 40, 32768, 32768, 128, 0)
+    rec = 40 * 512 * 32768 * 4
+    assert rec > ops.QAT_P_ABSMAX_MAX_BYTES
+    assert ops.workspace_bytes(lv, ops.QAT_P_QUANT, 1) == ops.workspace_bytes(lv, 0, 1)
+    assert ops.workspace_bytes(big, ops.QAT_P_QUANT, 1) == (ops.workspace_bytes(big, 0, 1)
+                                                            + up(24 * 72 * 4608 * 4))
     assert ops.workspace_bytes(d, 0, 2) == 0
 
 

@@ -67,6 +67,19 @@ def test_small_full_compare(name):
     assert_within(compare(gpu, ref), name)
 
 
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_full_compare_in_kernel_absmax(name):
+    # the same cases through the static-scratch backward, whose dK/dV kernel
+    # forms the P-quant absmax of each (query, 64-key group) itself (as the
+    # backward does for problems whose absmax record would exceed its bound)
+    w = SMALL[name]
+    print(f"case {name} (in-kernel absmax): {w}", flush=True)
+    inp = W.make_inputs(w)
+    gpu = run_gpu(w, inp, bwd_entry="noalloc")
+    ref = run_oracle(w, inp)
+    assert_within(compare(gpu, ref), name + " in-kernel absmax")
+
+
 def test_p_quant_off_gives_identical_outputs():
     w = BASE.with_(B=1, H=2, Nq=200, Nkv=150, seed=23)
     inp = W.make_inputs(w)
