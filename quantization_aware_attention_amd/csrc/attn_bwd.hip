@@ -12,18 +12,20 @@
 //  * dQ kernel: a workgroup of 4 waves owns 128 query rows; like the forward,
 //    each wave computes S^T = K Q^T and dP^T = V dO^T so every lane owns one
 //    query row (Q^T, dO^T stay in registers, K/V tiles stream through LDS);
-//    dQ^T = K^T dS^T reads K^T through ds_read_b64_tr_b16.  dQ does not use
-//    P^, so this kernel forms no P-quant scale.
+//    dQ^T = K^T dS^T reads K^T through ds_read_b64_tr_b16.  A lane holds a
+//    query row's 64-key group, so this kernel can record the P-quant absmax
+//    of every (row, group) for the dK/dV kernel (when that record is kept).
 //  * dK/dV kernel: a workgroup of 8 waves owns 128 keys (two P groups);
 //    each wave keeps its 32 keys' K^T (and V^T) in registers and computes
 //    S = Q K^T (and dP = dO V^T) with one lane per key, so P^ and dS are
 //    already the operands of dV^T = dO^T P^ and dK^T = Q^T dS (Q and dO
 //    tiles go through LDS, read row-major for S/dP and transposed for dV/dK).
 //    Half the waves accumulate dV, half dK, so each holds one accumulator.
-//    A query's 64-key P group spans the 32 keys of two waves: each reduces
-//    its half over lanes, the two exchange the halves through LDS across the
-//    workgroup barrier, and the P^ and dV of a block follow one iteration
-//    later.  Nothing of size Nq x Nkv leaves the kernels.
+//    A query's 64-key P group spans the 32 keys of two waves: the kernel
+//    reads the dQ kernel's absmax record, or (AMX, when the record would be
+//    too large to keep) each wave reduces its half over lanes, the two
+//    exchange the halves through LDS across the workgroup barrier, and the
+//    P^ and dV of a block follow one iteration later.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -454,12 +456,14 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 // SIMD: while one wave waits on an MFMA or an LDS read the other issues, and
 // the two waves' vector work runs under each other's matrix work.
 // The absmax of a (query, 64-key group) needs the keys of two P waves (kw,
-// kw ^ 1): each publishes its 32-key maximum per query of block i, and after
-// the barrier both form the group's scales and quantize P(i), read back
-// from LDS.
+// kw ^ 1).  With the dQ kernel's record, wave 1 stages its scale pairs with
+// the block.  Without it (AMX), each P wave publishes its 32-key maximum
+// per query of block i, and after the barrier both form the group's scales
+// and quantize P(i), read back from LDS.
 // Iteration i (one workgroup barrier at its end):
-//   P wave:  S(i+1) MFMAs; P(i) to LDS and its 32-key maxima; scales and
-//            P^ of block i-1; dV MFMAs of block i-1;
+//   P wave:  S(i+1) MFMAs; P(i) to LDS; P^ and dV MFMAs of block i, or
+//            (AMX) the 32-key maxima of block i, and scales, P^ and dV
+//            MFMAs of block i-1;
 //   dS wave: dP(i) MFMAs; vector work of block i-1 (P(i-1) from LDS, written
 //            in iteration i-1); dK MFMAs of block i-1;
 //   all:     block i+2 (loaded in iteration i-1) written to LDS slot
