@@ -32,7 +32,8 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 qat::Shape shape_of(const qat_attn_dims& d) { return qat::Shape{d.B, d.H, d.Nq, d.Nkv, d.D, d.dtype}; }
 
 struct Layout {
-  size_t delta = 0, amax = 0, part = 0, kpart = 0, kmean = 0, ksm = 0, qh = 0, kh = 0, vh = 0, qs = 0, ks = 0, total = 0;
+  size_t delta = 0, amax = 0, part = 0, kpart = 0, kmean = 0, ksm = 0, qh = 0, kh = 0, vh = 0, qs = 0, ks = 0;
+  size_t q8 = 0, k8 = 0, total = 0;
   bool side = false;   // the absmax record is part of the workspace
 };
 
@@ -79,6 +80,10 @@ Layout layout(const qat_attn_dims& d, uint32_t flags, int pass, bool full = true
     off += align_up(BH * d.Nq * sizeof(float));
     L.ks = off;
     off += align_up(BH * d.Nkv * sizeof(float));
+    L.q8 = off;
+    off += align_up(BH * d.Nq * d.D);
+    L.k8 = off;
+    off += align_up(BH * d.Nkv * d.D);
   }
   L.total = off;
   return L;
@@ -141,10 +146,10 @@ int prepare_inputs(const qat_attn_dims& d, const Layout& L, uint32_t flags, cons
   if (flags & QAT_QKV_QUANT) {
     float* qs = reinterpret_cast<float*>(ws + L.qs);
     float* ks = reinterpret_cast<float*>(ws + L.ks);
-    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nq, q, ws + L.qh, qs, nullptr, st));
-    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nkv, k, ws + L.kh, ks, kmean, st));
-    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nkv, v, ws + L.vh, nullptr, nullptr, st));
-    *in = qat::Inputs{ws + L.qh, ws + L.kh, ws + L.vh, nullptr, qs, ks, qat::IN_QKS, kmean};
+    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nq, q, ws + L.qh, qs, nullptr, ws + L.q8, st));
+    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nkv, k, ws + L.kh, ks, kmean, ws + L.k8, st));
+    QAT_TRY(qat::launch_token_quant(d.dtype, d.D, BH * d.Nkv, v, ws + L.vh, nullptr, nullptr, nullptr, st));
+    *in = qat::Inputs{ws + L.qh, ws + L.kh, ws + L.vh, nullptr, qs, ks, qat::IN_QKS, kmean, ws + L.q8, ws + L.k8};
   }
   return QAT_OK;
 }
@@ -161,7 +166,7 @@ qat::Inputs prepared_inputs(const Layout& L, uint32_t flags, const void* q, cons
   }
   if (flags & QAT_QKV_QUANT)
     in = qat::Inputs{ws + L.qh, ws + L.kh, ws + L.vh, nullptr, reinterpret_cast<float*>(ws + L.qs),
-                     reinterpret_cast<float*>(ws + L.ks), qat::IN_QKS, in.k_mean};
+                     reinterpret_cast<float*>(ws + L.ks), qat::IN_QKS, in.k_mean, ws + L.q8, ws + L.k8};
   return in;
 }
 

@@ -38,6 +38,8 @@ struct FwdArgs {
   const float* v_scale;   // IN_VFP8: [BH, D]
   const float* q_scale;   // IN_QKS: [BH, Nq]
   const float* k_scale;   // IN_QKS: [BH, Nkv]
+  const uint8_t* q8;      // IN_QKS: e4m3 code bytes of Q and K (S^T on the fp8 MFMA)
+  const uint8_t* k8;
   void* o;
   void* o_hp;
   float* lse;
@@ -300,6 +302,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   static_assert(IN != IN_VFP8, "fp8 V uses fwd_f8v_kernel");
   constexpr bool QKS = IN == IN_QKS;
   constexpr int TILE = FWD_BN * D * 2;
+  constexpr int QKB = QKS ? 1 : 2;   // bytes per Q / K element in LDS: e4m3 codes with per-token scales
   constexpr int NDB = D / 32;
   constexpr int NKS = D / 16;
   constexpr int FQF = PQ >= 0 ? PQ : 0;
@@ -307,10 +310,10 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   // fragments in flight ahead of their MFMAs: five (no spills; six spilled
   // and ran slower), four with per-token codes (which need more registers)
   constexpr int PP_AHEAD = QKS ? 4 : 5;
-  __shared__ __attribute__((aligned(16))) char kbuf[2][TILE];
+  __shared__ __attribute__((aligned(16))) char kbuf[2][FWD_BN * D * QKB];
   __shared__ __attribute__((aligned(16))) char vbuf[2][TILE];
   __shared__ __attribute__((aligned(16))) float ks_s[3][FWD_BN];   // IN_QKS: key scales of K(t)
-  __shared__ __attribute__((aligned(16))) char qbuf[PP_BM * D * 2];   // the block's Q rows
+  __shared__ __attribute__((aligned(16))) char qbuf[PP_BM * D * QKB];   // the block's Q rows
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int grp = w >> 2;
@@ -325,10 +328,17 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   const uint16_t* kp = (const uint16_t*)a.k + (size_t)bh * Nkv * D;
   const uint16_t* vp = (const uint16_t*)a.v + (size_t)bh * Nkv * D;
 
+  const uint8_t* k8p = QKS ? a.k8 + (size_t)bh * Nkv * D : nullptr;
   {   // Q rows [qb, qb + PP_BM) into LDS (rows past Nq repeat the last row)
-    TileCopy<D, PP_BM, 8> qcopy;
-    qcopy.init(wave_id(), lane);
-    qcopy.issue(qbuf, qp, qb, Nq);
+    if constexpr (QKS) {
+      CodeCopy<D, PP_BM, 8, true> qcopy;
+      qcopy.init(wave_id(), lane);
+      qcopy.issue(qbuf, a.q8 + (size_t)bh * Nq * D, qb, Nq);
+    } else {
+      TileCopy<D, PP_BM, 8> qcopy;
+      qcopy.init(wave_id(), lane);
+      qcopy.issue(qbuf, qp, qb, Nq);
+    }
   }
   // exponent scale of this row; a zero per-token Q scale (all-zero row, every
   // score 0) is raised to the smallest normal so that masked scores stay -inf
@@ -338,8 +348,14 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 
   const int kv_end = CAUSAL ? min(Nkv, qb + PP_BM) : Nkv;
   const int T = (kv_end + FWD_BN - 1) / FWD_BN;
-  TileCopy<D, FWD_BN, 4> copy;   // used by group 0 only
+  TileCopy<D, FWD_BN, 4> copy;   // used by group 0 only (K and V, or V only)
   copy.init(wave_id() & 3, lane);
+  CodeCopy<D, FWD_BN, 4, true> kcopy8;   // IN_QKS: K codes
+  if constexpr (QKS) kcopy8.init(wave_id() & 3, lane);
+  auto issue_k = [&](int t) __attribute__((always_inline)) {
+    if constexpr (QKS) kcopy8.issue(kbuf[t & 1], k8p, t * FWD_BN, Nkv);
+    else copy.issue(kbuf[t & 1], kp, t * FWD_BN, Nkv);
+  };
   float ksreg = 0.0f;
 
   float m_used = -INFINITY, l_part = 0.0f;
@@ -380,17 +396,27 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   // The MFMA phase as one stream of single-fragment steps: NPV steps of
   // P@V (a V fragment feeding the O and O_hp MFMAs of a 16-key by 32-column
   // block), then for each k-step of S^T = K Q^T a Q fragment and the two K
-  // fragments (one MFMA each, against the last Q fragment).  Step f reads the
-  // fragment of step f + PP_AHEAD; scheduling fences keep that order, so every
-  // MFMA finds its LDS operand already loaded.
-  constexpr int NFR = NPV + 3 * NKS;
+  // fragments (one MFMA each, against the last Q fragment).  With per-token
+  // codes a k-step spans 64 d on the fp8 MFMA and every operand is two
+  // 16-byte halves, so the step order is Q, Q, K0, K0 (MFMA), K1, K1 (MFMA).
+  // Step f reads the fragment of step f + PP_AHEAD; scheduling fences keep
+  // that order, so every MFMA finds its LDS operand already loaded.
+  constexpr int NSS = QKS ? 6 * (D / 64) : 3 * NKS;   // S^T steps
+  constexpr int NFR = NPV + NSS;
   auto fetch = [&](const char* Vt, const char* Kt, int f) __attribute__((always_inline)) {
     if (f < NPV) return lds_tr8<D>(Vt, (f / NDB) * 16, (f % NDB) * 32, lane);
-    const int k = f - NPV, ks = k / 3, part = k % 3;
-    if (part == 0) return lds_row8<D>(qbuf, w * 32 + l32, 2 * ks + g);
-    return lds_row8<D>(Kt, (part - 1) * 32 + l32, 2 * ks + g);
+    const int k = f - NPV;
+    if constexpr (QKS) {   // e4m3 codes: chunk 4ks + 2g + half of the row, d = 64ks + 32g + 0..31
+      const int ks = k / 6, part = k % 6, obj = part >> 1, chunk = 4 * ks + 2 * g + (part & 1);
+      if (obj == 0) return lds_f8row<D>(qbuf, w * 32 + l32, chunk);
+      return lds_f8row<D>(Kt, (obj - 1) * 32 + l32, chunk);
+    } else {
+      const int ks = k / 3, part = k % 3;
+      if (part == 0) return lds_row8<D>(qbuf, w * 32 + l32, 2 * ks + g);
+      return lds_row8<D>(Kt, (part - 1) * 32 + l32, 2 * ks + g);
+    }
   };
-  s16x8 qcur;
+  s16x8 qcur, qcur2, kcur;
   auto step = [&](const s16x8& frag, int f) __attribute__((always_inline)) {
     if (f < NPV) {   // O^T += V^T P^T, k-step kk, column block db
       const int kk = f / NDB, db = f % NDB, kb = kk >> 1, o8 = 8 * (kk & 1);
@@ -403,13 +429,22 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
         o_acc[db] = DT::mfma(frag, bhp, o_acc[db]);
       }
     } else {          // S^T = K Q^T, k-step ks
-      const int k = f - NPV, part = k % 3;
+      const int k = f - NPV;
       if (k == 0) {
         s[0] = (f32x16){};
         s[1] = (f32x16){};
       }
-      if (part == 0) qcur = frag;
-      else s[part - 1] = DT::mfma(frag, qcur, s[part - 1]);
+      if constexpr (QKS) {
+        const int part = k % 6;
+        if (part == 0) qcur = frag;
+        else if (part == 1) qcur2 = frag;
+        else if (part == 2 || part == 4) kcur = frag;
+        else s[(part - 3) >> 1] = mfma_e4m3(kcur, frag, qcur, qcur2, s[(part - 3) >> 1]);
+      } else {
+        const int part = k % 3;
+        if (part == 0) qcur = frag;
+        else s[part - 1] = DT::mfma(frag, qcur, s[part - 1]);
+      }
     }
   };
   auto mfma_phase = [&](int t) __attribute__((always_inline)) {
@@ -516,7 +551,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 
   // prologue: K(0) (and its scales) resident before phase 0
   if (T > 0 && grp == 0) {
-    copy.issue(kbuf[0], kp, 0, Nkv);
+    issue_k(0);
     if constexpr (QKS) {
       if (tid < FWD_BN) ksreg = tid < Nkv ? ksp[tid] : 0.0f;
     }
@@ -542,7 +577,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       const int t = ph_i >> 1;
       if (grp == 0) {
         if (t + 1 < T) {
-          copy.issue(kbuf[(t + 1) & 1], kp, (t + 1) * FWD_BN, Nkv);
+          issue_k(t + 1);
           if constexpr (QKS) {
             const int key = (t + 1) * FWD_BN + tid;
             if (tid < FWD_BN) ksreg = key < Nkv ? ksp[key] : 0.0f;
@@ -633,6 +668,7 @@ hipError_t launch_fwd(const Shape& s, const Inputs& in, float sm_scale, bool cau
   FwdArgs a;
   a.q = in.q; a.k = in.k; a.v = in.v;
   a.v_scale = in.v_scale; a.q_scale = in.q_scale; a.k_scale = in.k_scale;
+  a.q8 = (const uint8_t*)in.q8; a.k8 = (const uint8_t*)in.k8;
   a.o = o; a.o_hp = o_hp; a.lse = lse;
   a.Nq = s.Nq; a.Nkv = s.Nkv;
   a.c = sm_scale * LOG2E;

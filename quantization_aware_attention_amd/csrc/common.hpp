@@ -342,9 +342,41 @@ __device__ __forceinline__ s16x8 e5m2x8_to_f16(int lo, int hi) {
   return __builtin_bit_cast(s16x8, (u32x4){a, b, c, d});
 }
 
+// LDS tile of 8-bit codes that is read row-major (the fp8 MFMA operands of
+// per-token Q and K codes): rows of D bytes in 16-byte chunks, chunk c of row
+// R stored at c ^ f8_swz(R).  Eight consecutive rows reading one chunk each
+// fall on eight distinct 16-byte bank groups of a 128-byte line, and so do
+// the even and the odd rows of sixteen consecutive ones.
+template <int D>
+__device__ __forceinline__ int f8_swz(int row) {
+  if constexpr (D == 128) return (row ^ (row >> 3)) & 7;
+  else return (row ^ (row >> 2)) & 3;
+}
+template <int D>
+__device__ __forceinline__ int f8_off(int row, int chunk) {
+  return row * D + ((chunk ^ f8_swz<D>(row)) << 4);
+}
+// One 16-byte chunk of a row of codes (half of an fp8 MFMA operand).
+template <int D>
+__device__ __forceinline__ s16x8 lds_f8row(const char* tile, int row, int chunk) {
+  return *reinterpret_cast<const s16x8*>(tile + f8_off<D>(row, chunk));
+}
+// C += A B over 64 k of e4m3 codes (v_mfma_f32_32x32x64_f8f6f4, unit block
+// scales): lane l holds row or column l % 32 and, in its two 16-byte halves,
+// the 32 codes k = 32 (l / 32) + 0..31 of the k step, for A and B alike.
+__device__ __forceinline__ f32x16 mfma_e4m3(const s16x8& alo, const s16x8& ahi, const s16x8& blo,
+                                            const s16x8& bhi, const f32x16& c) {
+  const u32x4 a0 = __builtin_bit_cast(u32x4, alo), a1 = __builtin_bit_cast(u32x4, ahi);
+  const u32x4 b0 = __builtin_bit_cast(u32x4, blo), b1 = __builtin_bit_cast(u32x4, bhi);
+  const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
 // Asynchronous copy of [BN x D] 8-bit code tiles from HBM into the vc_swz
-// layout (global_load_lds_dwordx4; same scheme as TileCopy).
-template <int D, int BN, int NW>
+// layout (ROWMAJOR: the f8_swz layout) with global_load_lds_dwordx4 (same
+// scheme as TileCopy).
+template <int D, int BN, int NW, bool ROWMAJOR = false>
 struct CodeCopy {
   static constexpr int CPR = D / 16;                   // 16-byte chunks per row
   static constexpr int ROWS_PER_KIB = 1024 / D;
@@ -359,7 +391,7 @@ struct CodeCopy {
 #pragma unroll
     for (int u = 0; u < PER_WAVE; ++u) {
       const int row = (wave * PER_WAVE + u) * ROWS_PER_KIB + lane / CPR;
-      const int chunk = (lane % CPR) ^ vc_swz<D>(row);
+      const int chunk = (lane % CPR) ^ (ROWMAJOR ? f8_swz<D>(row) : vc_swz<D>(row));
       off[u] = (uint32_t)(row * D + chunk * 16);
     }
   }

@@ -27,6 +27,8 @@ struct Inputs {
   const float* k_scale;   // IN_QKS
   int mode;
   const float* k_mean;    // K smoothing: the mean subtracted from K (dQ correction), or null
+  const void* q8;         // IN_QKS: e4m3 code bytes of Q and K [BH, N, D] (the fp8 MFMA operands of S)
+  const void* k8;
 };
 
 // pfmt: -1 = P not quantized, 0 = e4m3fn, 1 = e5m2
@@ -34,9 +36,10 @@ hipError_t launch_fwd(const Shape& s, const Inputs& in, float sm_scale, bool cau
                       void* o, void* o_hp, float* lse, hipStream_t st);
 
 // Per-token e4m3 fake quant: x [rows, D] -> xhat [rows, D] (same dtype); with
-// scale_out the code values and the per-row scales are stored separately.
+// scale_out the code values and the per-row scales are stored separately, and
+// with codes8 also the e4m3 code bytes [rows, D].
 hipError_t launch_token_quant(int dtype, int D, long rows, const void* x, void* xhat, float* scale_out,
-                              const float* shift, hipStream_t st);
+                              const float* shift, void* codes8, hipStream_t st);
 
 // K smoothing: mean[D] = dtype-rounded mean of K [rows, D] over all rows
 // (part: KMEAN_BLOCKS x D fp32 scratch); with k_smooth, also K - mean rounded

@@ -18,12 +18,14 @@ namespace qat {
 // so that x^ = code * s stays exact for the attention kernels; otherwise
 // x^ = fp32(code * s) is rounded to the storage dtype.
 // With `shift` (K smoothing) the row first becomes x - shift[d], rounded to
-// the dtype: the smoothed K the attention sees.
+// the dtype: the smoothed K the attention sees.  With `codes8` (split only)
+// the e4m3 code bytes are stored as well, for the fp8 MFMAs of S.
 template <class DT, int D>
 __global__ __launch_bounds__(256) void token_quant_kernel(const uint16_t* __restrict__ x,
                                                           uint16_t* __restrict__ xhat,
                                                           float* __restrict__ scale_out, long rows,
-                                                          const float* __restrict__ shift) {
+                                                          const float* __restrict__ shift,
+                                                          uint8_t* __restrict__ codes8) {
   constexpr int EPL = D / 16;   // elements per lane
   const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
@@ -51,32 +53,44 @@ __global__ __launch_bounds__(256) void token_quant_kernel(const uint16_t* __rest
   const FqScale fs = fq_scale<0>(amax);
   const bool split = scale_out != nullptr;
   const FqScale unit = {1.0f, fs.r};   // code value times 1: the code itself
-  uint32_t outw[EPL / 2];
+  uint32_t outw[EPL / 2], code2[EPL / 2];
 #pragma unroll
   for (int e = 0; e < EPL; e += 2) {
-    f32x2 xq = fq_pair<0>(v[e], v[e + 1], split ? unit : fs);
-    if (fs.r == 0.0f) xq = (f32x2){0.0f, 0.0f};   // zero group: +0, not -0
+    f32x2 xq = fq_pair<0>(v[e], v[e + 1], split ? unit : fs, &code2[e / 2]);
+    if (fs.r == 0.0f) {   // zero group: +0, not -0
+      xq = (f32x2){0.0f, 0.0f};
+      code2[e / 2] = 0u;
+    }
     outw[e / 2] = DT::pack2(xq[0], xq[1]);
   }
   if (!valid) return;
   if (split && sub == 0) scale_out[row] = fs.s;
+  if (codes8) {   // two codes per conversion, in its low 16 bits
+    uint32_t cw[EPL / 4];
+#pragma unroll
+    for (int h = 0; h < EPL / 4; ++h) cw[h] = (code2[2 * h] & 0xFFFFu) | (code2[2 * h + 1] << 16);
+    uint8_t* cdst = codes8 + row * D + sub * EPL;
+    if constexpr (EPL == 8) *reinterpret_cast<u32x2*>(cdst) = (u32x2){cw[0], cw[1]};
+    else *reinterpret_cast<uint32_t*>(cdst) = cw[0];
+  }
   uint16_t* dst = xhat + row * D + sub * EPL;
   if constexpr (EPL == 8) *reinterpret_cast<u32x4*>(dst) = (u32x4){outw[0], outw[1], outw[2], outw[3]};
   else *reinterpret_cast<u32x2*>(dst) = (u32x2){outw[0], outw[1]};
 }
 
 hipError_t launch_token_quant(int dtype, int D, long rows, const void* x, void* xhat, float* scale_out,
-                              const float* shift, hipStream_t st) {
+                              const float* shift, void* codes8, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   dim3 grid((unsigned)((rows + 15) / 16));
   const uint16_t* xi = (const uint16_t*)x;
   uint16_t* xo = (uint16_t*)xhat;
+  uint8_t* c8 = (uint8_t*)codes8;
   if (dtype == 0) {
-    if (D == 128) hipLaunchKernelGGL((token_quant_kernel<BF16, 128>), grid, dim3(256), 0, st, xi, xo, scale_out, rows, shift);
-    else hipLaunchKernelGGL((token_quant_kernel<BF16, 64>), grid, dim3(256), 0, st, xi, xo, scale_out, rows, shift);
+    if (D == 128) hipLaunchKernelGGL((token_quant_kernel<BF16, 128>), grid, dim3(256), 0, st, xi, xo, scale_out, rows, shift, c8);
+    else hipLaunchKernelGGL((token_quant_kernel<BF16, 64>), grid, dim3(256), 0, st, xi, xo, scale_out, rows, shift, c8);
   } else {
-    if (D == 128) hipLaunchKernelGGL((token_quant_kernel<FP16, 128>), grid, dim3(256), 0, st, xi, xo, scale_out, rows, shift);
-    else hipLaunchKernelGGL((token_quant_kernel<FP16, 64>), grid, dim3(256), 0, st, xi, xo, scale_out, rows, shift);
+    if (D == 128) hipLaunchKernelGGL((token_quant_kernel<FP16, 128>), grid, dim3(256), 0, st, xi, xo, scale_out, rows, shift, c8);
+    else hipLaunchKernelGGL((token_quant_kernel<FP16, 64>), grid, dim3(256), 0, st, xi, xo, scale_out, rows, shift, c8);
   }
   return hipGetLastError();
 }

@@ -115,7 +115,9 @@ def test_workspace_layout():
     amax = up(2 * 3 * 3 * 100 * 4)            # P-quant absmax record: ceil(130 / 64) = 3 groups
     assert ops.workspace_bytes(d, 0, 1) == delta + part
     assert ops.workspace_bytes(d, ops.QAT_P_QUANT, 1) == delta + amax + part
-    qkv = up(6 * 100 * 128 * 2) + 2 * up(6 * 130 * 128 * 2) + up(6 * 100 * 4) + up(6 * 130 * 4)
+    # Q, K code values and V^ (dtype), per-token scales, e4m3 code bytes of Q and K
+    qkv = (up(6 * 100 * 128 * 2) + 2 * up(6 * 130 * 128 * 2) + up(6 * 100 * 4) + up(6 * 130 * 4)
+           + up(6 * 100 * 128) + up(6 * 130 * 128))
     assert ops.workspace_bytes(d, ops.QAT_P_QUANT | ops.QAT_QKV_QUANT, 0) == qkv
     assert ops.workspace_bytes(d, ops.QAT_P_QUANT | ops.QAT_QKV_QUANT, 1) == delta + amax + part + qkv
     # K smoothing (both passes): mean partial sums [256, D] and the mean [D] fp32, and
