@@ -91,6 +91,8 @@ struct BwdArgs {
   const float* v_scale;   // IN_VFP8
   const float* q_scale;   // IN_QKS
   const float* k_scale;   // IN_QKS
+  const uint8_t* q8;      // IN_QKS: e4m3 code bytes of Q and K (S on the fp8 MFMA)
+  const uint8_t* k8;
   const void* dout;
   const float* lse;
   const float* delta;
@@ -178,25 +180,31 @@ constexpr int DQ_BN = 64;
 
 // SMK: K smoothing, dQ += sm_scale rowsum(dS) k_mean (a separate instance, so
 // that the plain kernel is not burdened with the extra row sum)
+// IN_QKS: S on the fp8 MFMA from the e4m3 code bytes, whose K tiles take
+// LDS beside the 16-bit K tiles of dQ; the workgroup is then eight waves (256
+// rows, one per CU), since two four-wave workgroups would not fit one CU's LDS.
 template <class DT, int D, bool CAUSAL, int PQ, int IN, bool SMK>
-__global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(IN == IN_QKS ? 512 : 256, IN == IN_QKS ? 1 : 2) void dq_kernel(BwdArgs a) {
   constexpr bool VFP8 = IN == IN_VFP8;
   constexpr bool QKS = IN == IN_QKS;
   constexpr int TILE = DQ_BN * D * 2;
   constexpr int NDB = D / 32;
   constexpr int NKS = D / 16;
+  constexpr int NW = QKS ? 8 : 4;    // waves
+  constexpr int BM = NW * 32;        // query rows per workgroup
   __shared__ __attribute__((aligned(16))) char smem[2][2][TILE];   // [buffer][K, V]
   __shared__ __attribute__((aligned(16))) float ks_s[2][DQ_BN];     // IN_QKS: key scales
+  __shared__ __attribute__((aligned(16))) char k8_s[QKS ? 2 : 1][QKS ? DQ_BN * D : 16];   // IN_QKS: K codes
   // IN_VFP8: the next tile's V codes, copied HBM -> LDS by DMA
   constexpr int VC_BYTES = VFP8 ? DQ_BN * D : 16;
   constexpr int VC_PER_THREAD = DQ_BN * D / (256 * 16);   // 16-byte chunks per thread
   __shared__ __attribute__((aligned(16))) char vc_s[VC_BYTES];
 
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 5, l32 = lane & 31;
-  const int ntq = (a.Nq + DQ_BM - 1) / DQ_BM;
+  const int ntq = (a.Nq + BM - 1) / BM;
   int bh, rank;   // causal: the longest rows (last blocks) first
   work_unit(blockIdx.x, gridDim.x, ntq, CAUSAL, &bh, &rank);
-  const int qb = (CAUSAL ? ntq - 1 - rank : rank) * DQ_BM;
+  const int qb = (CAUSAL ? ntq - 1 - rank : rank) * BM;
   const int q0 = qb + w * 32;
   const int qi = q0 + l32;
   const int lane_g4 = 4 * g, lane_dq = 4 * g - l32;   // mask terms (key - kv0 - c, key - qi + q0 - kv0 - c)
@@ -207,11 +215,20 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   const uint8_t* vp = (const uint8_t*)a.v + (size_t)bh * Nkv * D * (VFP8 ? 1 : 2);
   const float* vsc = VFP8 ? a.v_scale + (size_t)bh * D : nullptr;
 
-  s16x8 qf[NKS], dof[NKS];
+  // Q^T (B operand of S^T = K Q^T): 16-bit values, or with per-token codes
+  // the e4m3 bytes d = 64 ks + 32 g + 0..31 of the row in two 16-byte halves
+  s16x8 qf[QKS ? 2 * (D / 64) : NKS], dof[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     const bool ok = qi < Nq;
-    qf[ks] = ok ? *reinterpret_cast<const s16x8*>(qp + (size_t)qi * D + 16 * ks + 8 * g) : (s16x8){};
+    if constexpr (QKS) {
+      if (ks < 2 * (D / 64))
+        qf[ks] = ok ? *reinterpret_cast<const s16x8*>(a.q8 + ((size_t)bh * Nq + qi) * D + 64 * (ks >> 1) + 32 * g +
+                                                      16 * (ks & 1))
+                    : (s16x8){};
+    } else {
+      qf[ks] = ok ? *reinterpret_cast<const s16x8*>(qp + (size_t)qi * D + 16 * ks + 8 * g) : (s16x8){};
+    }
     dof[ks] = ok ? *reinterpret_cast<const s16x8*>(dop + (size_t)qi * D + 16 * ks + 8 * g) : (s16x8){};
   }
   const float Mi = qi < Nq ? a.lse[(size_t)bh * Nq + qi] * LOG2E : 0.0f;
@@ -275,10 +292,16 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   // completed, so the decode needs no barrier.  Key scales take a register
   // detour.
   float ksreg = 0.0f;
-  TileCopy<D, DQ_BN, 4> copy;
+  TileCopy<D, DQ_BN, NW> copy;
   copy.init(w, lane);
+  constexpr int K8W = DQ_BN * D / 1024 < NW ? DQ_BN * D / 1024 : NW;   // waves copying the K code tile
+  CodeCopy<D, DQ_BN, K8W, true> kcopy8;
+  if constexpr (QKS) kcopy8.init(w % K8W, lane);
   auto issue_tile = [&](int t, int buf) {
     copy.issue(smem[buf][0], kp, t * DQ_BN, Nkv);
+    if constexpr (QKS) {
+      if (w < K8W) kcopy8.issue(k8_s[QKS ? buf : 0], a.k8 + (size_t)bh * Nkv * D, t * DQ_BN, Nkv);
+    }
     if constexpr (VFP8) {
 #pragma unroll
       for (int u = 0; u < VC_PER_THREAD; ++u) {
@@ -312,7 +335,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
     }
   };
 
-  const int kv_end = CAUSAL ? min(Nkv, qb + DQ_BM) : Nkv;
+  const int kv_end = CAUSAL ? min(Nkv, qb + BM) : Nkv;
   const int ntiles = (kv_end + DQ_BN - 1) / DQ_BN;
   if (ntiles > 0) {
     issue_tile(0, 0);
@@ -332,9 +355,16 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = (f32x16){};
       dp[kb] = (f32x16){};
+      if constexpr (QKS) {   // K codes against Q codes, 64 d per MFMA
+        const char* K8t = k8_s[QKS ? buf : 0];
+#pragma unroll
+        for (int ks = 0; ks < D / 64; ++ks)
+          s[kb] = mfma_e4m3(lds_f8row<D>(K8t, kb * 32 + l32, 4 * ks + 2 * g),
+                            lds_f8row<D>(K8t, kb * 32 + l32, 4 * ks + 2 * g + 1), qf[2 * ks], qf[2 * ks + 1], s[kb]);
+      }
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        s[kb] = DT::mfma(lds_row8<D>(Kt, kb * 32 + l32, 2 * ks + g), qf[ks], s[kb]);
+        if constexpr (!QKS) s[kb] = DT::mfma(lds_row8<D>(Kt, kb * 32 + l32, 2 * ks + g), qf[ks], s[kb]);
         if constexpr (VFP8) dp[kb] = FP16::mfma(lds_row8<D>(Vt, kb * 32 + l32, 2 * ks + g), dof[ks], dp[kb]);
         else dp[kb] = DT::mfma(lds_row8<D>(Vt, kb * 32 + l32, 2 * ks + g), dof[ks], dp[kb]);
       }
@@ -1136,8 +1166,9 @@ __global__ __launch_bounds__(256) void dkdv_merge_kernel(BwdArgs a, int nkb) {
 template <class DT, int D, bool CAUSAL, int PQ, int IN>
 struct DqK {
   static void run(dim3 g, const BwdArgs& a, hipStream_t st) {
-    if (a.k_mean) hipLaunchKernelGGL((dq_kernel<DT, D, CAUSAL, PQ, IN, true>), g, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((dq_kernel<DT, D, CAUSAL, PQ, IN, false>), g, dim3(256), 0, st, a);
+    const dim3 blk(IN == IN_QKS ? 512 : 256);
+    if (a.k_mean) hipLaunchKernelGGL((dq_kernel<DT, D, CAUSAL, PQ, IN, true>), g, blk, 0, st, a);
+    else hipLaunchKernelGGL((dq_kernel<DT, D, CAUSAL, PQ, IN, false>), g, blk, 0, st, a);
   }
 };
 template <class DT, int D, bool CAUSAL, int PQ, int IN>
@@ -1194,6 +1225,7 @@ static BwdArgs make_args(const Shape& s, const Inputs& in, const void* dout, con
   BwdArgs a = {};
   a.q = in.q; a.k = in.k; a.v = in.v;
   a.v_scale = in.v_scale; a.q_scale = in.q_scale; a.k_scale = in.k_scale;
+  a.q8 = (const uint8_t*)in.q8; a.k8 = (const uint8_t*)in.k8;
   a.dout = dout; a.lse = lse; a.delta = delta;
   a.Nq = s.Nq; a.Nkv = s.Nkv; a.NG = (s.Nkv + P_GROUP - 1) / P_GROUP;
   a.k_mean = in.k_mean;
@@ -1212,7 +1244,8 @@ hipError_t launch_bwd_dq(const Shape& s, const Inputs& in, const void* dout, con
     a.o_hp = o_hp;
     a.delta_out = delta;
   }
-  dim3 grid(((s.Nq + DQ_BM - 1) / DQ_BM) * s.B * s.H);
+  const int bm = in.mode == IN_QKS ? 2 * DQ_BM : DQ_BM;   // rows per workgroup (dq_kernel's BM)
+  dim3 grid(((s.Nq + bm - 1) / bm) * s.B * s.H);
   return pick_all<DqK>(s, grid, a, causal, pfmt, in.mode, st);
 }
 
