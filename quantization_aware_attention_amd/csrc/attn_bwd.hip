@@ -577,12 +577,13 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
   constexpr int CPR = D / 8;                // 16-byte chunks per row
   constexpr int CHUNKS = DPR_BQ * CPR;      // chunks per tensor and block
   constexpr int NCH = 2 * CHUNKS / 512;     // staged chunks per thread (Q and dO together)
-  constexpr int NST = NKS + 2 * NDB;        // MFMA steps of a wave per iteration
   constexpr int NGRP = 8;                   // fenced groups per iteration
-  constexpr int GSZ = NST / NGRP;           // MFMAs per group
   constexpr int AHEAD = 2;                  // MFMA steps whose LDS operand is in flight
-  static_assert(NST % NGRP == 0 && NCH >= 1 && 2 * CHUNKS % 512 == 0, "shape");
+  static_assert(NCH >= 1 && 2 * CHUNKS % 512 == 0, "shape");
   __shared__ __attribute__((aligned(16))) char q_s[DPR_SLOTS][TILE];
+  // IN_QKS: the block's e4m3 Q code bytes (the P wave's fp8 MFMA operand of
+  // S), converted from the staged Q code values as they are written
+  __shared__ __attribute__((aligned(16))) char q8_s[QKS ? DPR_SLOTS : 1][QKS ? DPR_BQ * D : 16];
   __shared__ __attribute__((aligned(16))) char do_s[DPR_SLOTS][TILE];
   __shared__ __attribute__((aligned(16))) float m_s[DPR_SLOTS][DPR_BQ];
   __shared__ __attribute__((aligned(16))) float d_s[DPR_SLOTS][DPR_BQ];
@@ -697,6 +698,19 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
     for (int j = 0; j < NCH; ++j) {
       const int within = st_within(j), row = within / CPR, ch = within % CPR;
       *reinterpret_cast<u32x4*>((st_tensor(j) ? do_s[slot] : q_s[slot]) + tile_off<D>(row, ch)) = stg[j];
+      if constexpr (QKS) {   // the chunk's 8 Q code values (exact e4m3 values) as code bytes, for the fp8 S
+        if (!st_tensor(j)) {
+          float f[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] = DT::to_f32((uint16_t)(stg[j][e >> 1] >> (16 * (e & 1))));
+          int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+          lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+          int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+          hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+          *reinterpret_cast<u32x2*>(q8_s[QKS ? slot : 0] + f8_off<D>(row, ch >> 1) + 8 * (ch & 1)) =
+              (u32x2){(uint32_t)lo, (uint32_t)hi};
+        }
+      }
       if constexpr (VFP8) {
         if (st_tensor(j)) {   // the row's CPR chunks sit in CPR consecutive lanes
           const f32x4 va = *reinterpret_cast<const f32x4*>(&vs_s[8 * ch]);
@@ -752,6 +766,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
     for (int k = tid; k < 2 * DPR_SLOTS * WPS; k += 512) {
       const int t = k / (DPR_SLOTS * WPS), sl = (k / WPS) % DPR_SLOTS, o = (k % WPS) * 16;
       if (sl >= z0) *reinterpret_cast<u32x4*>((t ? do_s[sl] : q_s[sl]) + o) = (u32x4){0u, 0u, 0u, 0u};
+      if constexpr (QKS) {
+        if (sl >= z0 && !t && o < DPR_BQ * D) *reinterpret_cast<u32x4*>(q8_s[QKS ? sl : 0] + o) = (u32x4){0u, 0u, 0u, 0u};
+      }
       if constexpr (VFP8) {
         if (sl >= z0 && t) *reinterpret_cast<u32x4*>(dos_s[VFP8 ? sl : 0] + o) = (u32x4){0u, 0u, 0u, 0u};
       }
@@ -782,8 +799,17 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
   // one wave role for the whole kernel: R = 0 P wave, R = 1 dS wave
   auto run = [&](auto ROLE) __attribute__((always_inline)) {
     constexpr int R = decltype(ROLE)::value;
+    // per-token codes: the P wave forms S on the fp8 MFMA, 64 d per step
+    constexpr bool F8S = QKS && R == 0;
+    constexpr int NSS = F8S ? 2 * (D / 64) : NKS;   // score steps (fp8: two 16-byte halves per MFMA)
+    constexpr int NST = NSS + 2 * NDB;              // MFMA-operand steps per iteration
+    constexpr int GMAX = (NSS + 3) / 4 > (2 * NDB + 3) / 4 ? (NSS + 3) / 4 : (2 * NDB + 3) / 4;
+    // steps [gb(j), gb(j + 1)) run in fenced group j: the score steps in
+    // groups 0-3, the accumulator steps in groups 4-7
+    auto gb = [](int j) { return j < 4 ? j * NSS / 4 : NSS + (j - 4) * (2 * NDB) / 4; };
     // K^T (P wave) or V^T (dS wave) of this wave's 32 keys: lane holds key
-    // kj, d = 16 ks + 8 g .. +7
+    // kj, d = 16 ks + 8 g .. +7; fp8 K^T: half h holds the code bytes
+    // d = 64 (h / 2) + 32 g + 16 (h % 2) .. +15
     s16x8 kv[NKS];
     {
       const bool ok = kj < Nkv;
@@ -791,7 +817,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
       for (int ks = 0; ks < NKS; ++ks) {
         kv[ks] = (s16x8){};
         if (!ok) continue;
-        if constexpr (R == 0) {
+        if constexpr (F8S) {
+          if (ks < NSS)
+            kv[ks] = *reinterpret_cast<const s16x8*>(a.k8 + ((size_t)bh * Nkv + kj) * D + 64 * (ks >> 1) + 32 * g +
+                                                     16 * (ks & 1));
+        } else if constexpr (R == 0) {
           const uint16_t* kp = (const uint16_t*)a.k + (size_t)bh * Nkv * D;
           kv[ks] = *reinterpret_cast<const s16x8*>(kp + (size_t)kj * D + 16 * ks + 8 * g);
         } else if constexpr (VFP8) {   // the e5m2 codes as fp16 values (exact); v_scale is on dO
@@ -835,7 +865,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
     auto tiles = [&](auto SLOTc, const char*& X, const char*& Y) __attribute__((always_inline)) {
       constexpr int SL = decltype(SLOTc)::value;   // slot of block i
       if constexpr (R == 0) {   // dV of block i - 1 (AMX) or i
-        X = q_s[(SL + 1) & (DPR_SLOTS - 1)];
+        X = F8S ? q8_s[QKS ? (SL + 1) & (DPR_SLOTS - 1) : 0] : q_s[(SL + 1) & (DPR_SLOTS - 1)];
         Y = do_s[AMX ? (SL + DPR_SLOTS - 1) & (DPR_SLOTS - 1) : SL];
       } else {
         X = VFP8 ? dos_s[VFP8 ? SL : 0] : do_s[SL];
@@ -843,17 +873,27 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
       }
     };
     auto fetch = [&](const char* X, const char* Y, int st) __attribute__((always_inline)) {
-      if (st < NKS) return lds_row8<D>(X, l32, 2 * st + g);
-      const int k = st - NKS, h = k / NDB, db = k % NDB;
+      if (st < NSS) {
+        if constexpr (F8S) return lds_f8row<D>(X, l32, 4 * (st >> 1) + 2 * g + (st & 1));
+        else return lds_row8<D>(X, l32, 2 * st + g);
+      }
+      const int k = st - NSS, h = k / NDB, db = k % NDB;
       return lds_tr8<D>(Y, 16 * h, 32 * db, lane);
     };
+    s16x8 qlo8;   // fp8 S: the first half of the Q operand
     auto step = [&](const s16x8& frag, int st, f32x16& SO) __attribute__((always_inline)) {
-      if (st < NKS) {
+      if (st < NSS) {
         if (st == 0) SO = (f32x16){};
-        if constexpr (VFP8 && R == 1) SO = FP16::mfma(frag, kv[st], SO);
-        else SO = DT::mfma(frag, kv[st], SO);
+        if constexpr (F8S) {
+          if ((st & 1) == 0) qlo8 = frag;
+          else SO = mfma_e4m3(qlo8, frag, kv[st - 1], kv[st], SO);
+        } else if constexpr (VFP8 && R == 1) {
+          SO = FP16::mfma(frag, kv[st], SO);
+        } else {
+          SO = DT::mfma(frag, kv[st], SO);
+        }
       } else {
-        const int k = st - NKS, h = k / NDB, db = k % NDB;
+        const int k = st - NSS, h = k / NDB, db = k % NDB;
         const s16x8 o = __builtin_bit_cast(s16x8, (u32x4){op[4 * h], op[4 * h + 1], op[4 * h + 2], op[4 * h + 3]});
         acc[db] = DT::mfma(frag, o, acc[db]);
       }
@@ -1067,8 +1107,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
       for (int j = 0; j < NGRP; ++j) {
 #pragma unroll
-        for (int k = 0; k < GSZ; ++k) {
-          const int st = j * GSZ + k;
+        for (int k = 0; k < GMAX; ++k) {
+          const int st = gb(j) + k;
+          if (st >= gb(j + 1)) continue;
           const s16x8 cur = ring[st % AHEAD];
           if (st + AHEAD < NST) ring[st % AHEAD] = fetch(X, Y, st + AHEAD);
           step(cur, st, SO);
@@ -1092,9 +1133,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
 
     // P wave: S(0) before the first iteration
     if (R == 0 && NB > 0 && active(0)) {
-      const char* X0 = q_s[0];
+      const char* X0 = F8S ? q8_s[0] : q_s[0];
 #pragma unroll
-      for (int st = 0; st < NKS; ++st) step(fetch(X0, X0, st), st, sb[0]);
+      for (int st = 0; st < NSS; ++st) step(fetch(X0, X0, st), st, sb[0]);
     }
     for (int i = 0; i <= NB; i += DPR_SLOTS) {
       static_assert(DPR_SLOTS == 4, "the loop is unrolled by the slot count");
