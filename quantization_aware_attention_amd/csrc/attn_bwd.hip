@@ -177,6 +177,15 @@ __device__ __forceinline__ Pow2Scale pow2_scale(float m) {
 
 constexpr int DQ_BM = 128;
 constexpr int DQ_BN = 64;
+// Waves of a dQ workgroup (32 query rows each).  Eight (256 rows, one
+// workgroup per CU) load each K/V tile once for twice the rows: the DiT image
+// dQ 0.397 -> 0.376 ms.  Causal launches keep four (finer blocks balance the
+// unequal row lengths better: causal LM dQ 0.237 -> 0.247 ms with eight), and
+// so does fp8 V (its code-tile copies are laid out for four waves).  Per-token
+// codes need eight (LDS for the K code tiles; see dq_kernel).
+constexpr int dq_waves(int in, bool causal) {
+  return in == IN_QKS ? 8 : (in == IN_VFP8 || causal ? 4 : 8);
+}
 
 // SMK: K smoothing, dQ += sm_scale rowsum(dS) k_mean (a separate instance, so
 // that the plain kernel is not burdened with the extra row sum)
@@ -184,13 +193,13 @@ constexpr int DQ_BN = 64;
 // LDS beside the 16-bit K tiles of dQ; the workgroup is then eight waves (256
 // rows, one per CU), since two four-wave workgroups would not fit one CU's LDS.
 template <class DT, int D, bool CAUSAL, int PQ, int IN, bool SMK>
-__global__ __launch_bounds__(IN == IN_QKS ? 512 : 256, IN == IN_QKS ? 1 : 2) void dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(dq_waves(IN, CAUSAL) * 64, dq_waves(IN, CAUSAL) == 8 ? 1 : 2) void dq_kernel(BwdArgs a) {
   constexpr bool VFP8 = IN == IN_VFP8;
   constexpr bool QKS = IN == IN_QKS;
   constexpr int TILE = DQ_BN * D * 2;
   constexpr int NDB = D / 32;
   constexpr int NKS = D / 16;
-  constexpr int NW = QKS ? 8 : 4;    // waves
+  constexpr int NW = dq_waves(IN, CAUSAL);   // waves
   constexpr int BM = NW * 32;        // query rows per workgroup
   __shared__ __attribute__((aligned(16))) char smem[2][2][TILE];   // [buffer][K, V]
   __shared__ __attribute__((aligned(16))) float ks_s[2][DQ_BN];     // IN_QKS: key scales
@@ -1207,7 +1216,7 @@ __global__ __launch_bounds__(256) void dkdv_merge_kernel(BwdArgs a, int nkb) {
 template <class DT, int D, bool CAUSAL, int PQ, int IN>
 struct DqK {
   static void run(dim3 g, const BwdArgs& a, hipStream_t st) {
-    const dim3 blk(IN == IN_QKS ? 512 : 256);
+    const dim3 blk(dq_waves(IN, CAUSAL) * 64);
     if (a.k_mean) hipLaunchKernelGGL((dq_kernel<DT, D, CAUSAL, PQ, IN, true>), g, blk, 0, st, a);
     else hipLaunchKernelGGL((dq_kernel<DT, D, CAUSAL, PQ, IN, false>), g, blk, 0, st, a);
   }
@@ -1285,7 +1294,7 @@ hipError_t launch_bwd_dq(const Shape& s, const Inputs& in, const void* dout, con
     a.o_hp = o_hp;
     a.delta_out = delta;
   }
-  const int bm = in.mode == IN_QKS ? 2 * DQ_BM : DQ_BM;   // rows per workgroup (dq_kernel's BM)
+  const int bm = dq_waves(in.mode, causal) * 32;   // rows per workgroup (dq_kernel's BM)
   dim3 grid(((s.Nq + bm - 1) / bm) * s.B * s.H);
   return pick_all<DqK>(s, grid, a, causal, pfmt, in.mode, st);
 }

@@ -121,7 +121,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 // offsets are fixed for the whole loop; each copy only adds a wave-uniform
 // base.  Rows past `nrows` are clamped to the last valid row (finite data;
 // the kernels mask those rows).  Each of the NW waves issues
-// (BN*D*2/1024)/NW instructions.
+// (BN*D*2/1024)/NW instructions.  Only the offset of the wave's first KiB is
+// held: the swizzles split into a part of the KiB index and a part of the
+// lane (disjoint bits), so KiB u of the wave is that offset with the chunk
+// bits XORed by a wave-uniform term, plus u KiB.
 template <int D, int BN, int NW>
 struct TileCopy {
   static constexpr int ROW_BYTES = D * 2;
@@ -130,18 +133,17 @@ struct TileCopy {
   static constexpr int KIB = BN * ROW_BYTES / 1024;
   static constexpr int PER_WAVE = KIB / NW;
   static_assert(KIB % NW == 0, "tile must split evenly over the waves");
-  uint32_t off[PER_WAVE];   // byte offset of this lane's source chunk inside the tile
-  int wave;                 // wave index (uniform)
+  uint32_t off0;   // byte offset of this lane's source chunk in the wave's first KiB
+  int wave;        // wave index (uniform)
 
   __device__ __forceinline__ void init(int wave_uniform, int lane) {
     wave = wave_uniform;
-#pragma unroll
-    for (int u = 0; u < PER_WAVE; ++u) {
-      const int blk = wave * PER_WAVE + u;
-      const int row = blk * ROWS_PER_KIB + lane / CPR;
-      const int chunk = (lane % CPR) ^ swz<D>(row);
-      off[u] = (uint32_t)(row * ROW_BYTES + chunk * 16);
-    }
+    const int row = wave * PER_WAVE * ROWS_PER_KIB + lane / CPR;
+    off0 = (uint32_t)(row * ROW_BYTES + (((lane % CPR) ^ swz<D>(row)) * 16));
+  }
+  __device__ __forceinline__ uint32_t offset(int u) const {
+    const int b0 = wave * PER_WAVE * ROWS_PER_KIB, bu = b0 + u * ROWS_PER_KIB;
+    return (off0 ^ (uint32_t)((swz<D>(bu) ^ swz<D>(b0)) << 4)) + u * 1024;
   }
   // Copy rows [row0, row0 + BN) of src ([nrows x D]) into lds_tile.
   __device__ __forceinline__ void issue(char* lds_tile, const uint16_t* src, int row0, int nrows) const {
@@ -149,7 +151,7 @@ struct TileCopy {
     const bool full = row0 + BN <= nrows;
 #pragma unroll
     for (int u = 0; u < PER_WAVE; ++u) {
-      uint32_t o = off[u];
+      uint32_t o = offset(u);
       if (!full) {   // tail tile: clamp the row, keep the column
         const int row = (int)(o / ROW_BYTES);
         const int r = min(row0 + row, nrows - 1) - row0;
@@ -383,24 +385,25 @@ struct CodeCopy {
   static constexpr int KIB = BN * D / 1024;
   static constexpr int PER_WAVE = KIB / NW;
   static_assert(KIB % NW == 0, "tile must split evenly over the waves");
-  uint32_t off[PER_WAVE];
+  uint32_t off0;   // as in TileCopy: the first KiB's offset, the others derived
   int wave;
 
+  __device__ __forceinline__ static int sw(int row) { return ROWMAJOR ? f8_swz<D>(row) : vc_swz<D>(row); }
   __device__ __forceinline__ void init(int wave_uniform, int lane) {
     wave = wave_uniform;
-#pragma unroll
-    for (int u = 0; u < PER_WAVE; ++u) {
-      const int row = (wave * PER_WAVE + u) * ROWS_PER_KIB + lane / CPR;
-      const int chunk = (lane % CPR) ^ (ROWMAJOR ? f8_swz<D>(row) : vc_swz<D>(row));
-      off[u] = (uint32_t)(row * D + chunk * 16);
-    }
+    const int row = wave * PER_WAVE * ROWS_PER_KIB + lane / CPR;
+    off0 = (uint32_t)(row * D + (((lane % CPR) ^ sw(row)) * 16));
+  }
+  __device__ __forceinline__ uint32_t offset(int u) const {
+    const int b0 = wave * PER_WAVE * ROWS_PER_KIB, bu = b0 + u * ROWS_PER_KIB;
+    return (off0 ^ (uint32_t)((sw(bu) ^ sw(b0)) << 4)) + u * 1024;
   }
   __device__ __forceinline__ void issue(char* lds_tile, const uint8_t* src, int row0, int nrows) const {
     const char* base = reinterpret_cast<const char*>(src + (size_t)row0 * D);
     const bool full = row0 + BN <= nrows;
 #pragma unroll
     for (int u = 0; u < PER_WAVE; ++u) {
-      uint32_t o = off[u];
+      uint32_t o = offset(u);
       if (!full) {
         const int row = (int)(o / D);
         const int r = min(row0 + row, nrows - 1) - row0;
