@@ -180,11 +180,13 @@ constexpr int DQ_BN = 64;
 // Waves of a dQ workgroup (32 query rows each).  Eight (256 rows, one
 // workgroup per CU) load each K/V tile once for twice the rows: the DiT image
 // dQ 0.397 -> 0.376 ms.  Causal launches keep four (finer blocks balance the
-// unequal row lengths better: causal LM dQ 0.237 -> 0.247 ms with eight), and
-// so does fp8 V (its code-tile copies are laid out for four waves).  Per-token
-// codes need eight (LDS for the K code tiles; see dq_kernel).
+// unequal row lengths better: causal LM dQ 0.237 -> 0.247 ms with eight),
+// and so does fp8 V (its workgroups see few key tiles, 8 at the
+// cross-attention shape, and two per CU overlap one's prologue with the
+// other's tiles: dQ 0.213 -> 0.234 ms with eight).  Per-token codes need
+// eight (LDS for the K code tiles; see dq_kernel).
 constexpr int dq_waves(int in, bool causal) {
-  return in == IN_QKS ? 8 : (in == IN_VFP8 || causal ? 4 : 8);
+  return in == IN_QKS ? 8 : (causal || in == IN_VFP8 ? 4 : 8);
 }
 
 // SMK: K smoothing, dQ += sm_scale rowsum(dS) k_mean (a separate instance, so
@@ -206,7 +208,9 @@ __global__ __launch_bounds__(dq_waves(IN, CAUSAL) * 64, dq_waves(IN, CAUSAL) == 
   __shared__ __attribute__((aligned(16))) char k8_s[QKS ? 2 : 1][QKS ? DQ_BN * D : 16];   // IN_QKS: K codes
   // IN_VFP8: the next tile's V codes, copied HBM -> LDS by DMA
   constexpr int VC_BYTES = VFP8 ? DQ_BN * D : 16;
-  constexpr int VC_PER_THREAD = DQ_BN * D / (256 * 16);   // 16-byte chunks per thread
+  constexpr int VC_KIB = DQ_BN * D / 1024;                    // KiB of a code tile
+  constexpr int VCW = VC_KIB < dq_waves(IN, CAUSAL) ? VC_KIB : dq_waves(IN, CAUSAL);   // waves copying it
+  constexpr int VC_PER_THREAD = VC_KIB / VCW;                 // 16-byte chunks per thread of those waves
   __shared__ __attribute__((aligned(16))) char vc_s[VC_BYTES];
 
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 5, l32 = lane & 31;
@@ -296,8 +300,9 @@ __global__ __launch_bounds__(dq_waves(IN, CAUSAL) * 64, dq_waves(IN, CAUSAL) == 
 
   // K tiles (and V, unless fp8) go HBM -> LDS directly, double-buffered.  fp8
   // V codes go HBM -> LDS by DMA too, into one 8-bit tile in plain row order:
-  // chunk u of a thread is the 16 bytes at P = (4u + wave) KiB + 16 lane,
-  // and the same thread decodes exactly those bytes after its own copies
+  // chunk u of a thread of the VCW copying waves is the 16 bytes at
+  // P = (VCW u + wave) KiB + 16 lane, and the same thread decodes exactly
+  // those bytes after its own copies
   // completed, so the decode needs no barrier.  Key scales take a register
   // detour.
   float ksreg = 0.0f;
@@ -314,7 +319,8 @@ __global__ __launch_bounds__(dq_waves(IN, CAUSAL) * 64, dq_waves(IN, CAUSAL) == 
     if constexpr (VFP8) {
 #pragma unroll
       for (int u = 0; u < VC_PER_THREAD; ++u) {
-        const int blk = u * 4 + w, P = blk * 1024 + lane * 16;
+        if (w >= VCW) break;
+        const int blk = u * VCW + w, P = blk * 1024 + lane * 16;
         const int key = min(t * DQ_BN + P / D, Nkv - 1);   // tail rows repeat the last key (masked)
         __builtin_amdgcn_global_load_lds((const void*)(vp + (size_t)key * D + P % D),
                                          (lds_void*)(vc_s + blk * 1024), 16, 0, 0);
@@ -331,7 +337,8 @@ __global__ __launch_bounds__(dq_waves(IN, CAUSAL) * 64, dq_waves(IN, CAUSAL) == 
     if constexpr (VFP8) {   // the code values themselves as fp16 (exact: an e5m2 code is an fp16's high byte)
 #pragma unroll
       for (int u = 0; u < VC_PER_THREAD; ++u) {
-        const int P = (u * 4 + w) * 1024 + lane * 16, row = P / D, c0 = P % D;
+        if (w >= VCW) break;
+        const int P = (u * VCW + w) * 1024 + lane * 16, row = P / D, c0 = P % D;
         const u32x4 codes = *reinterpret_cast<const u32x4*>(vc_s + P);
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)   // 8 codes -> one 16-byte chunk of the fp16 tile

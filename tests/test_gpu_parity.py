@@ -29,6 +29,7 @@ SMALL = {
     "bf16_d64_e5m2": BASE.with_(B=1, H=2, Nq=257, Nkv=257, D=64, p_fmt="e5m2", seed=14),
     "bf16_qkv_quant": BASE.with_(B=1, H=2, Nq=190, Nkv=190, qkv_quant=True, seed=15),
     "bf16_fp8v_nkv500": W.WORKLOADS["cross_fp8v"].with_(B=1, H=2, Nq=150, Nkv=500, seed=16),
+    "bf16_fp8v_d64_ragged": W.WORKLOADS["cross_fp8v"].with_(B=1, H=2, Nq=300, Nkv=200, D=64, seed=29),
     "bf16_k_offset": W.WORKLOADS["dit_image"].with_(H=2, Nq=256, Nkv=256, seed=17),
     "fp16_causal_d128": BASE.with_(B=1, H=2, Nq=129, Nkv=129, dtype="fp16", causal=True, seed=18),
     "one_key": BASE.with_(B=1, H=1, Nq=70, Nkv=1, seed=19),
