@@ -248,13 +248,18 @@ __device__ __forceinline__ f32x2 fq_pair(float x0, float x1, FqScale q, uint32_t
 // (low word first), so no register clearing or masking is needed.
 template <int FMT>
 __device__ __forceinline__ f32x4 fq_quad(const float x[4], const FqScale q[4]) {
+  // The first conversion writes the low half of its destination and keeps the
+  // high half of its third operand, which the second conversion overwrites:
+  // passing a product that dies there lets the destination take its register
+  // (no copy of a live value into a fresh one).
+  const float v0 = x[0] * q[0].r, v1 = x[1] * q[1].r, v2 = x[2] * q[2].r, v3 = x[3] * q[3].r;
   int pk;
   if constexpr (FMT == 0) {
-    pk = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] * q[0].r, x[1] * q[1].r, __builtin_bit_cast(int, x[0]), false);
-    pk = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] * q[2].r, x[3] * q[3].r, pk, true);
+    pk = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, __builtin_bit_cast(int, v0), false);
+    pk = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, pk, true);
   } else {
-    pk = __builtin_amdgcn_cvt_pk_bf8_f32(x[0] * q[0].r, x[1] * q[1].r, __builtin_bit_cast(int, x[0]), false);
-    pk = __builtin_amdgcn_cvt_pk_bf8_f32(x[2] * q[2].r, x[3] * q[3].r, pk, true);
+    pk = __builtin_amdgcn_cvt_pk_bf8_f32(v0, v1, __builtin_bit_cast(int, v0), false);
+    pk = __builtin_amdgcn_cvt_pk_bf8_f32(v2, v3, pk, true);
   }
   f32x2 lo, hi;
   if constexpr (FMT == 0) {
@@ -271,13 +276,14 @@ __device__ __forceinline__ f32x4 fq_quad(const float x[4], const FqScale q[4]) {
 // for callers that feed the codes themselves to an fp8 MFMA.
 template <int FMT>
 __device__ __forceinline__ int fq_codes4(const float x[4], float r) {
-  int pk;
+  const float v0 = x[0] * r, v1 = x[1] * r, v2 = x[2] * r, v3 = x[3] * r;
+  int pk;   // (third operand of the first conversion: as in fq_quad)
   if constexpr (FMT == 0) {
-    pk = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] * r, x[1] * r, 0, false);
-    pk = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] * r, x[3] * r, pk, true);
+    pk = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, __builtin_bit_cast(int, v0), false);
+    pk = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, pk, true);
   } else {
-    pk = __builtin_amdgcn_cvt_pk_bf8_f32(x[0] * r, x[1] * r, 0, false);
-    pk = __builtin_amdgcn_cvt_pk_bf8_f32(x[2] * r, x[3] * r, pk, true);
+    pk = __builtin_amdgcn_cvt_pk_bf8_f32(v0, v1, __builtin_bit_cast(int, v0), false);
+    pk = __builtin_amdgcn_cvt_pk_bf8_f32(v2, v3, pk, true);
   }
   return pk;
 }
