@@ -707,11 +707,13 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
     }
     if (v_live) stv = v_src[min(q0 + l32, Nq - 1)];
   };
-  // (slot: compile-time b % DPR_SLOTS, so the LDS addresses fold into offsets)
-  auto write_tiles = [&](auto SLOTc) __attribute__((always_inline)) {
+  // chunks [jlo, jhi) of the staged block (slot: compile-time b % DPR_SLOTS,
+  // so the LDS addresses fold into offsets)
+  auto write_tiles = [&](auto SLOTc, int jlo, int jhi) __attribute__((always_inline)) {
     constexpr int slot = decltype(SLOTc)::value;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
+      if (j < jlo || j >= jhi) continue;
       const int within = st_within(j), row = within / CPR, ch = within % CPR;
       *reinterpret_cast<u32x4*>((st_tensor(j) ? do_s[slot] : q_s[slot]) + tile_off<D>(row, ch)) = stg[j];
       if constexpr (QKS) {   // the chunk's 8 Q code values (exact e4m3 values) as code bytes, for the fp8 S
@@ -808,8 +810,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
   }
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  if (NB > 0) { load_stage(0); write_tiles(I0{}); write_vec(0, I0{}); }
-  if (NB > 1) { load_stage(1); write_tiles(I1{}); write_vec(1, I1{}); }
+  if (NB > 0) { load_stage(0); write_tiles(I0{}, 0, NCH); write_vec(0, I0{}); }
+  if (NB > 1) { load_stage(1); write_tiles(I1{}, 0, NCH); write_vec(1, I1{}); }
   if (NB > 2) load_stage(2);
 
   // one wave role for the whole kernel: R = 0 P wave, R = 1 dS wave
@@ -1139,9 +1141,15 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
           for (int w4 = 0; w4 < 4; ++w4) op[(j == zlo ? 0 : 4) + w4] = 0u;
         }
-        if (j == 0 && stw) write_tiles(std::integral_constant<int, (SL + 2) & (DPR_SLOTS - 1)>{});
-        if (j == 1 && stw) write_vec(i + 2, std::integral_constant<int, (SL + 2) & (DPR_SLOTS - 1)>{});
-        if (j == 2 && stl) load_stage(i + 3);
+        // Block i+2 goes to LDS in groups 4 (chunk 0: the Q tile, or both
+        // tiles at D = 64) and 6 (the dO tile), whose own LDS traffic is the
+        // lightest (group 0 carries the dS wave's P and Delta reads and the
+        // P wave's M and scale reads); block i+3 is loaded after both.
+        using W2 = std::integral_constant<int, (SL + 2) & (DPR_SLOTS - 1)>;
+        if (j == 4 && stw) write_tiles(W2{}, 0, NCH > 1 ? 1 : NCH);
+        if (j == 6 && stw && NCH > 1) write_tiles(W2{}, 1, NCH);
+        if (j == 1 && stw) write_vec(i + 2, W2{});
+        if (j == 7 && stl) load_stage(i + 3);
         __builtin_amdgcn_sched_barrier(0);
       }
       __syncthreads();
