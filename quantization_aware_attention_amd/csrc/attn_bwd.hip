@@ -513,7 +513,8 @@ __global__ __launch_bounds__(dq_waves(IN, CAUSAL) * 64, dq_waves(IN, CAUSAL) == 
 //   dS wave: dP(i) MFMAs; vector work of block i-1 (P(i-1) from LDS, written
 //            in iteration i-1); dK MFMAs of block i-1;
 //   all:     block i+2 (loaded in iteration i-1) written to LDS slot
-//            (i+2) % 4, block i+3 loaded into registers.
+//            (i+2) % 4 in the second half of the iteration, then block i+3
+//            loaded into the staging registers.
 // LDS slot reads in iteration i touch blocks i-1 .. i+1 only, so the slot
 // written in iteration i was last read in iteration i-1, before the barrier;
 // the P buffer and the maxima of parity i&1 are rewritten in iteration i+2,
