@@ -125,15 +125,20 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, copy_mib: int):
 
 
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources; HBM counter readings are valid only for the
-    kernels they were taken on."""
+    """Hash of the HIP sources with comments and blank lines left out; HBM
+    counter readings are valid only for the kernels they were taken on (an
+    edit of a comment does not change a kernel)."""
     import hashlib
+    import re
     root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "quantization_aware_attention_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(root)):
         if name.endswith((".hip", ".hpp", ".cpp")):
+            text = open(os.path.join(root, name), encoding="utf-8").read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)   # block comments (none sit inside strings here)
+            code = [re.sub(r"//.*$", "", line).rstrip() for line in text.splitlines()]
             h.update(name.encode())
-            h.update(open(os.path.join(root, name), "rb").read())
+            h.update("\n".join(line for line in code if line).encode())
     return h.hexdigest()[:16]
 
 
