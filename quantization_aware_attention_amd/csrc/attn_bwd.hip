@@ -580,6 +580,16 @@ constexpr int DPR_SLOTS = 4;   // LDS slots of Q/dO blocks
 
 // AMX (P quant only): the P waves form the group absmax themselves (above);
 // otherwise they read the absmax the dQ kernel recorded per (query, group).
+// Lanes of a 32-query score register with query offset c that the causal
+// mask hides in a wave's diagonal block: lane l (key l % 32 of the wave's
+// 32, query 4 (l / 32) + c of the block) when its key follows the query.
+constexpr uint64_t diag_lane_mask(int c) {
+  uint64_t m = 0;
+  for (int l = 0; l < 64; ++l)
+    if ((l & 31) - 4 * (l >> 5) > c) m |= 1ull << l;
+  return m;
+}
+
 template <class DT, int D, bool CAUSAL, int PQ, int IN, bool AMX>
 __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
   static_assert(!AMX || PQ >= 0, "in-kernel absmax is for P quant");
@@ -1078,18 +1088,22 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(BwdArgs a) {
     // registers are zero), since every MFMA output column belongs to one key
     // and those columns are never stored.  Only the causal diagonal block
     // needs a per-element mask: register r holds query q0 + 4g + c_r,
-    // c_r = 8(r/4) + r%4, so kj > q compares one per-lane value with a
-    // constant.  It runs unconditionally (a branch around it makes the
-    // register allocator copy S between the two paths); above the diagonal
-    // dq <= -32 masks nothing, below it the block is inactive anyway.
+    // c_r = 8(r/4) + r%4, and lane l the key k0w + l % 32.  With off = q0 -
+    // k0w (a multiple of 32, the same for the whole wave) a block before the
+    // wave's diagonal (off < 0) has every key past every query, the diagonal
+    // block (off = 0) masks the lanes with l % 32 - 4 (l / 32) > c_r, and later
+    // blocks mask nothing: so register r's mask over the 64 lanes is one of
+    // three wave-uniform 64-bit values, chosen by scalar instructions, and
+    // the select takes it as its lane condition (one vector instruction per
+    // register).  It runs unconditionally (a branch around it makes the
+    // register allocator copy S between the two paths).
     auto mask = [&](int i, f32x16& S) __attribute__((always_inline)) {
       if constexpr (CAUSAL) {
-        int dq = kj - qstart(i) - 4 * g;
-        asm volatile("" : "+v"(dq));   // keeps dq > c from becoming 16 loop-invariant bounds
+        const int off = qstart(i) - k0w;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int c = 8 * (r >> 2) + (r & 3);
-          S[r] = dq > c ? -INFINITY : S[r];
+          const uint64_t m = off < 0 ? ~0ull : (off == 0 ? diag_lane_mask(8 * (r >> 2) + (r & 3)) : 0ull);
+          S[r] = __builtin_amdgcn_inverse_ballot_w64(m) ? -INFINITY : S[r];
         }
       }
     };
