@@ -403,8 +403,24 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   // that order, so every MFMA finds its LDS operand already loaded.
   constexpr int NSS = QKS ? 6 * (D / 64) : 3 * NKS;   // S^T steps
   constexpr int NFR = NPV + NSS;
+  // Operand addresses formed once: the lane offsets of the V^T reads of
+  // k-step 0 per column block (k-step kk adds 16kk rows, a constant that the
+  // reads take as an immediate offset), and those of the wave's Q fragments,
+  // which never move.  Formed per read, they cost a vector add or two in
+  // front of each read of the MFMA phase.
+  int vt_lane[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) vt_lane[db][h] = tr8_off<D>(8 * h, db * 32, lane);
+  int q_lane[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) q_lane[ks] = tile_off<D>(w * 32 + l32, 2 * ks + g);
   auto fetch = [&](const char* Vt, const char* Kt, int f) __attribute__((always_inline)) {
-    if (f < NPV) return lds_tr8<D>(Vt, (f / NDB) * 16, (f % NDB) * 32, lane);
+    if (f < NPV) {
+      const char* vk = Vt + (f / NDB) * 16 * D * 2;
+      return lds_tr8_at(vk + vt_lane[f % NDB][0], vk + vt_lane[f % NDB][1]);
+    }
     const int k = f - NPV;
     if constexpr (QKS) {   // e4m3 codes: chunk 4ks + 2g + half of the row, d = 64ks + 32g + 0..31
       const int ks = k / 6, part = k % 6, obj = part >> 1, chunk = 4 * ks + 2 * g + (part & 1);
@@ -412,7 +428,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       return lds_f8row<D>(Kt, (obj - 1) * 32 + l32, chunk);
     } else {
       const int ks = k / 3, part = k % 3;
-      if (part == 0) return lds_row8<D>(qbuf, w * 32 + l32, 2 * ks + g);
+      if (part == 0) return *reinterpret_cast<const s16x8*>(qbuf + q_lane[ks]);
       return lds_row8<D>(Kt, (part - 1) * 32 + l32, 2 * ks + g);
     }
   };
@@ -454,8 +470,15 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     const char* Kt = kbuf[t & 1];
     if (do_pv && do_qk) {
       s16x8 ring[PP_AHEAD];
+      // lgkmcnt(0): nothing is outstanding here, but stating it lets the
+      // compiler count the reads below in order (it otherwise waited for all
+      // of them before the first MFMA); the fences keep them in step order
+      __builtin_amdgcn_s_waitcnt(0xC07F);
 #pragma unroll
-      for (int f = 0; f < PP_AHEAD; ++f) ring[f] = fetch(Vt, Kt, f);
+      for (int f = 0; f < PP_AHEAD; ++f) {
+        ring[f] = fetch(Vt, Kt, f);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int f = 0; f < NFR; ++f) {

@@ -99,17 +99,25 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // Within each 16-lane group the instruction hands lane i, slot s, element
 // i%4 of the 8 bytes read by lane 4s + i/4; so lane (4s + q) of the group
 // reads row (base + s), columns col0 + 16*(group%2) + 4q .. +3.
+// Byte offset in the tile of lane `lane`'s 8-byte read of rows row0..row0+7;
+// the second read of the step is at tr8_off(row0 + 8, ...).  Moving row0 by
+// a multiple of 16 moves the offset by as many rows (the swizzle depends on
+// the row's low four bits only).
 template <int D>
-__device__ __forceinline__ s16x8 lds_tr8(const char* tile, int row0, int col0, int lane) {
+__device__ __forceinline__ int tr8_off(int row0, int col0, int lane) {
   const int G = lane >> 4, i = lane & 15, g = lane >> 5;
   const int row = row0 + 4 * g + (i >> 2);
   const int col = col0 + 16 * (G & 1) + 4 * (i & 3);
-  const int chunk = col >> 3, within = (col & 7) * 2;
-  const char* p0 = tile + tile_off<D>(row, chunk) + within;
-  const char* p1 = tile + tile_off<D>(row + 8, chunk) + within;
+  return tile_off<D>(row, col >> 3) + (col & 7) * 2;
+}
+__device__ __forceinline__ s16x8 lds_tr8_at(const char* p0, const char* p1) {
   s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
   s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
   return (s16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+template <int D>
+__device__ __forceinline__ s16x8 lds_tr8(const char* tile, int row0, int col0, int lane) {
+  return lds_tr8_at(tile + tr8_off<D>(row0, col0, lane), tile + tr8_off<D>(row0 + 8, col0, lane));
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
