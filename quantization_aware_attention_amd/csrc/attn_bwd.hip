@@ -367,22 +367,54 @@ __global__ __launch_bounds__(dq_waves(IN, CAUSAL) * 64, dq_waves(IN, CAUSAL) == 
     const char* Kt = smem[buf][0];
     const char* Vt = smem[buf][1];
     f32x16 s[2], dp[2];
+    if constexpr (!QKS) {
+      // S and dP as one stream of single-fragment steps (step f: key block
+      // f / 2NKS, k-step (f % 2NKS) / 2, K for S or V for dP), each fragment
+      // read DQ_AHEAD steps before its MFMA (fenced; the explicit lgkmcnt(0),
+      // where nothing is outstanding, lets the compiler count the stream's
+      // reads in order, as in the forward's MFMA phase)
+      constexpr int NSD = 4 * NKS, DQ_AHEAD = 2;
+      auto fetch_sd = [&](int f) __attribute__((always_inline)) {
+        return lds_row8<D>((f & 1) ? Vt : Kt, (f / (2 * NKS)) * 32 + l32, 2 * ((f % (2 * NKS)) >> 1) + g);
+      };
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = (f32x16){};
-      dp[kb] = (f32x16){};
-      if constexpr (QKS) {   // K codes against Q codes, 64 d per MFMA
-        const char* K8t = k8_s[QKS ? buf : 0];
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = (f32x16){};
+        dp[kb] = (f32x16){};
+      }
+      s16x8 ring[DQ_AHEAD];
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+#pragma unroll
+      for (int f = 0; f < DQ_AHEAD; ++f) {
+        ring[f] = fetch_sd(f);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int f = 0; f < NSD; ++f) {
+        const s16x8 cur = ring[f % DQ_AHEAD];
+        if (f + DQ_AHEAD < NSD) ring[f % DQ_AHEAD] = fetch_sd(f + DQ_AHEAD);
+        __builtin_amdgcn_sched_barrier(0);
+        const int kb = f / (2 * NKS), ks = (f % (2 * NKS)) >> 1;
+        if (f & 1) {
+          if constexpr (VFP8) dp[kb] = FP16::mfma(cur, dof[ks], dp[kb]);
+          else dp[kb] = DT::mfma(cur, dof[ks], dp[kb]);
+        } else {
+          s[kb] = DT::mfma(cur, qf[ks], s[kb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {   // per-token codes: S from the K codes against the Q codes, 64 d per MFMA
+      const char* K8t = k8_s[QKS ? buf : 0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = (f32x16){};
+        dp[kb] = (f32x16){};
 #pragma unroll
         for (int ks = 0; ks < D / 64; ++ks)
           s[kb] = mfma_e4m3(lds_f8row<D>(K8t, kb * 32 + l32, 4 * ks + 2 * g),
                             lds_f8row<D>(K8t, kb * 32 + l32, 4 * ks + 2 * g + 1), qf[2 * ks], qf[2 * ks + 1], s[kb]);
-      }
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        if constexpr (!QKS) s[kb] = DT::mfma(lds_row8<D>(Kt, kb * 32 + l32, 2 * ks + g), qf[ks], s[kb]);
-        if constexpr (VFP8) dp[kb] = FP16::mfma(lds_row8<D>(Vt, kb * 32 + l32, 2 * ks + g), dof[ks], dp[kb]);
-        else dp[kb] = DT::mfma(lds_row8<D>(Vt, kb * 32 + l32, 2 * ks + g), dof[ks], dp[kb]);
+        for (int ks = 0; ks < NKS; ++ks) dp[kb] = DT::mfma(lds_row8<D>(Vt, kb * 32 + l32, 2 * ks + g), dof[ks], dp[kb]);
       }
     }
     const bool need_mask = (kv0 + DQ_BN > Nkv) || (CAUSAL && kv0 + DQ_BN - 1 > q0);

@@ -123,12 +123,16 @@ __device__ __forceinline__ s16x8 lds_tr8(const char* tile, int row0, int col0, i
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Asynchronous copy of [BN x D] 16-bit tiles from HBM into the swizzled LDS
-// layout with global_load_lds_dwordx4: every wave instruction fills one
+// layout with buffer_load_dwordx4 ... lds: every wave instruction fills one
 // contiguous KiB of LDS (lane l -> bytes 16l..16l+15), so lane l fetches the
 // global chunk that belongs at that LDS position.  The per-lane source
 // offsets are fixed for the whole loop; each copy only adds a wave-uniform
 // base.  Rows past `nrows` are clamped to the last valid row (finite data;
-// the kernels mask those rows).  Each of the NW waves issues
+// the kernels mask those rows).  The buffer resource spans the tile, so an
+// offset outside it would read zeros rather than fault.  (The compiler counts
+// the global_load_lds form as a flat access that may touch LDS, and while one
+// is in flight it waits for every LDS read with lgkmcnt(0), which serialises
+// an operand stream behind the latest read.)  Each of the NW waves issues
 // (BN*D*2/1024)/NW instructions.  Only the offset of the wave's first KiB is
 // held: the swizzles split into a part of the KiB index and a part of the
 // lane (disjoint bits), so KiB u of the wave is that offset with the chunk
@@ -157,6 +161,7 @@ struct TileCopy {
   __device__ __forceinline__ void issue(char* lds_tile, const uint16_t* src, int row0, int nrows) const {
     const char* base = reinterpret_cast<const char*>(src + (size_t)row0 * D);
     const bool full = row0 + BN <= nrows;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, KIB * 1024, 0x00020000);
 #pragma unroll
     for (int u = 0; u < PER_WAVE; ++u) {
       uint32_t o = offset(u);
@@ -165,8 +170,8 @@ struct TileCopy {
         const int r = min(row0 + row, nrows - 1) - row0;
         o = (uint32_t)(r * ROW_BYTES) + (o % ROW_BYTES);
       }
-      __builtin_amdgcn_global_load_lds((const void*)(base + o),
-                                       (lds_void*)(lds_tile + (wave * PER_WAVE + u) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds_tile + (wave * PER_WAVE + u) * 1024), 16, o, 0,
+                                               0, 0);
     }
   }
 };
@@ -390,7 +395,7 @@ __device__ __forceinline__ f32x16 mfma_e4m3(const s16x8& alo, const s16x8& ahi, 
 }
 
 // Asynchronous copy of [BN x D] 8-bit code tiles from HBM into the vc_swz
-// layout (ROWMAJOR: the f8_swz layout) with global_load_lds_dwordx4 (same
+// layout (ROWMAJOR: the f8_swz layout) with buffer_load_dwordx4 ... lds (same
 // scheme as TileCopy).
 template <int D, int BN, int NW, bool ROWMAJOR = false>
 struct CodeCopy {
@@ -415,6 +420,7 @@ struct CodeCopy {
   __device__ __forceinline__ void issue(char* lds_tile, const uint8_t* src, int row0, int nrows) const {
     const char* base = reinterpret_cast<const char*>(src + (size_t)row0 * D);
     const bool full = row0 + BN <= nrows;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, KIB * 1024, 0x00020000);
 #pragma unroll
     for (int u = 0; u < PER_WAVE; ++u) {
       uint32_t o = offset(u);
@@ -423,8 +429,8 @@ struct CodeCopy {
         const int r = min(row0 + row, nrows - 1) - row0;
         o = (uint32_t)(r * D) + (o % D);
       }
-      __builtin_amdgcn_global_load_lds((const void*)(base + o),
-                                       (lds_void*)(lds_tile + (wave * PER_WAVE + u) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds_tile + (wave * PER_WAVE + u) * 1024), 16, o, 0,
+                                               0, 0);
     }
   }
 };
