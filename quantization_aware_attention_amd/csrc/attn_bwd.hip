@@ -370,9 +370,7 @@ __global__ __launch_bounds__(dq_waves(IN, CAUSAL) * 64, dq_waves(IN, CAUSAL) == 
     if constexpr (!QKS) {
       // S and dP as one stream of single-fragment steps (step f: key block
       // f / 2NKS, k-step (f % 2NKS) / 2, K for S or V for dP), each fragment
-      // read DQ_AHEAD steps before its MFMA (fenced; the explicit lgkmcnt(0),
-      // where nothing is outstanding, lets the compiler count the stream's
-      // reads in order, as in the forward's MFMA phase)
+      // read DQ_AHEAD steps before its MFMA (fenced)
       constexpr int NSD = 4 * NKS, DQ_AHEAD = 2;
       auto fetch_sd = [&](int f) __attribute__((always_inline)) {
         return lds_row8<D>((f & 1) ? Vt : Kt, (f / (2 * NKS)) * 32 + l32, 2 * ((f % (2 * NKS)) >> 1) + g);
@@ -383,7 +381,6 @@ __global__ __launch_bounds__(dq_waves(IN, CAUSAL) * 64, dq_waves(IN, CAUSAL) == 
         dp[kb] = (f32x16){};
       }
       s16x8 ring[DQ_AHEAD];
-      __builtin_amdgcn_s_waitcnt(0xC07F);
 #pragma unroll
       for (int f = 0; f < DQ_AHEAD; ++f) {
         ring[f] = fetch_sd(f);

@@ -470,12 +470,8 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     const char* Kt = kbuf[t & 1];
     if (do_pv && do_qk) {
       s16x8 ring[PP_AHEAD];
-      // lgkmcnt(0): nothing is outstanding here, but stating it lets the
-      // compiler count the reads below in order (it otherwise waited for all
-      // of them before the first MFMA); the fences keep them in step order
-      __builtin_amdgcn_s_waitcnt(0xC07F);
 #pragma unroll
-      for (int f = 0; f < PP_AHEAD; ++f) {
+      for (int f = 0; f < PP_AHEAD; ++f) {   // fenced, so that they issue in step order
         ring[f] = fetch(Vt, Kt, f);
         __builtin_amdgcn_sched_barrier(0);
       }
