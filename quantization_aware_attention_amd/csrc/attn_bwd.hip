@@ -295,6 +295,12 @@ __global__ __launch_bounds__(dq_waves(IN, CAUSAL) * 64, dq_waves(IN, CAUSAL) == 
   f32x16 dq_acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dq_acc[db] = (f32x16){};
+  // lane offsets of the K^T reads of k-step 0 per column block (a k-step adds 16 rows: an immediate offset)
+  int kt_lane[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) kt_lane[db][h] = tr8_off<D>(8 * h, db * 32, lane);
   constexpr bool smooth = SMK;
   float ds_rowsum = 0.0f;   // this lane's half of sum_j dS_ij (K smoothing)
 
@@ -460,7 +466,14 @@ __global__ __launch_bounds__(dq_waves(IN, CAUSAL) * 64, dq_waves(IN, CAUSAL) == 
 #pragma unroll
         for (int r = 0; r < 16; ++r) ds_rowsum += p[kb][r] * __builtin_fmaf(dp[kb][r], dp_down, -Di);
     }
-    // dQ^T += K^T dS^T
+    // dQ^T += K^T dS^T, the K^T fragments read two steps ahead
+    auto fetch_kt = [&](int f) __attribute__((always_inline)) {
+      const char* kk16 = Kt + (f / NDB) * 16 * D * 2;
+      return lds_tr8_at(kk16 + kt_lane[f % NDB][0], kk16 + kt_lane[f % NDB][1]);
+    };
+    s16x8 kr[2];
+    kr[0] = fetch_kt(0);
+    kr[1] = fetch_kt(1);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int kb = kk >> 1, h = kk & 1;
@@ -485,8 +498,14 @@ __global__ __launch_bounds__(dq_waves(IN, CAUSAL) * 64, dq_waves(IN, CAUSAL) == 
       }
       const s16x8 ds_op = __builtin_bit_cast(s16x8, (u32x4){w4[0], w4[1], w4[2], w4[3]});
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        dq_acc[db] = DT::mfma(lds_tr8<D>(Kt, kk * 16, db * 32, lane), ds_op, dq_acc[db]);
+      for (int db = 0; db < NDB; ++db) {
+        const int f = kk * NDB + db;
+        const s16x8 cur = kr[f & 1];
+        if (f + 2 < 4 * NDB) kr[f & 1] = fetch_kt(f + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        dq_acc[db] = DT::mfma(cur, ds_op, dq_acc[db]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     }
     wait_vmem();
